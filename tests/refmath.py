@@ -1,0 +1,81 @@
+"""Second, independent routes to the oracle's results, used only to pin it.
+
+Each function here computes the same mathematical object as an oracle function
+by a different method: vectorised bit slicing instead of per-value unpacking,
+a dense float64 matrix product on dequantised values instead of per-block
+integer dots, a lexicographic sort instead of repeated arg-max selection.
+"""
+import numpy as np
+
+
+def unpack_np(packed, wbits, n):
+    """Vectorised unpack of a packed row (layout as in tests/golden/pack_layout.txt)."""
+    b = np.asarray(packed, np.uint8).reshape(-1)
+    if wbits == 8:
+        return b[:n].view(np.int8).astype(np.int64)
+    nb = n // 32
+    if wbits == 4:
+        blk = b[: nb * 16].reshape(nb, 16).astype(np.int64)
+        lo, hi = blk & 0xF, blk >> 4
+        vals = np.concatenate([lo, hi], axis=1)          # positions j and j+16
+        return (np.where(vals >= 8, vals - 16, vals)).reshape(-1)
+    if wbits == 2:
+        blk = b[: nb * 8].reshape(nb, 8).astype(np.int64)
+        fields = [(blk >> (2 * m)) & 3 for m in range(4)]  # positions j + 8m
+        vals = np.concatenate(fields, axis=1)
+        return (np.where(vals >= 2, vals - 4, vals)).reshape(-1)
+    raise ValueError(wbits)
+
+
+def row_bytes(n, wbits):
+    return n * wbits // 8
+
+
+def dequant_expert(blob, scales, hidden, ffn, wbits):
+    """Dense float64 gate, up [F, H] and down [H, F] matrices: scale[row] * q."""
+    rh, rf = row_bytes(hidden, wbits), row_bytes(ffn, wbits)
+    blob = np.asarray(blob, np.uint8)
+    gate = unpack_np(blob[: ffn * rh], wbits, ffn * hidden).reshape(ffn, hidden)
+    up = unpack_np(blob[ffn * rh: 2 * ffn * rh], wbits, ffn * hidden).reshape(ffn, hidden)
+    down = unpack_np(blob[2 * ffn * rh: 2 * ffn * rh + hidden * rf], wbits, hidden * ffn).reshape(hidden, ffn)
+    s = np.asarray(scales, np.float64)
+    return (gate * s[:ffn, None], up * s[ffn: 2 * ffn, None], down * s[2 * ffn:, None])
+
+
+def dequant_q8(q, d):
+    """Dequantised Q8_0 row: d[block] * q in float64."""
+    q = np.asarray(q, np.float64).reshape(-1, 32)
+    return (q * np.asarray(d, np.float64).reshape(-1, 1)).reshape(-1)
+
+
+def router_bruteforce(x, W, bias, E, G, Gk, k, rsf):
+    """Route by explicit sorting: group mask from a lexsort of group scores, then a
+    lexsort of (-c, index) over the unmasked experts."""
+    z = np.asarray(x, np.float64) @ np.asarray(W, np.float64).T       # [T, E]
+    s = 1.0 / (1.0 + np.exp(-z))
+    c = s + np.asarray(bias, np.float64)[None, :]
+    T = z.shape[0]
+    m = E // G
+    idx = np.zeros((T, k), np.int64)
+    w = np.zeros((T, k), np.float64)
+    for t in range(T):
+        cg = c[t].reshape(G, m)
+        if m == 1:
+            gs = cg[:, 0]
+        else:
+            srt = np.sort(cg, axis=1)
+            gs = srt[:, -1] + srt[:, -2]
+        gorder = np.lexsort((np.arange(G), -gs))
+        keep = np.zeros(E, bool)
+        for g in gorder[:Gk]:
+            keep[g * m:(g + 1) * m] = True
+        cand = np.nonzero(keep)[0]
+        order = cand[np.lexsort((cand, -c[t, cand]))]
+        idx[t] = order[:k]
+        sel = s[t, idx[t]]
+        w[t] = sel / sel.sum() * rsf
+    return idx, w, s
+
+
+def silu(v):
+    return v / (1.0 + np.exp(-v))
