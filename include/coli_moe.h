@@ -1,0 +1,169 @@
+/*
+ * coli_moe.h — C ABI of libcolimoe.so: one routed Mixture-of-Experts layer on
+ * an AMD Instinct MI355X (gfx950), in hand-written HIP kernels.
+ *
+ * The layer, as the Colibri pages state it:
+ *   - router: DeepSeek-V3-style sigmoid router, noaux_tc, routed_scaling_factor,
+ *     plus a shared expert (colibri-strix README, "What's implemented", router item);
+ *   - batch-union: every distinct expert of the batch is read once and applied to
+ *     every position routed to it (colibri-strix README, "What's implemented",
+ *     batch-union item; JustVugg/colibri README, "Never wait for the disk twice");
+ *   - quantised experts: int8 / packed int4 / packed int2 weights with per-row
+ *     scales, dequantised on use (colibri-strix README, "What's implemented",
+ *     quantization kernels item), multiplied with Q8_0-style int8 activations by
+ *     integer dots (same section, integer-dot kernels item).
+ * The pages leave the router's group rule, the bit layouts and the rounding
+ * rules open; the readings this library implements are spelled out below.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library allocates no device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *     enqueued asynchronously; no call synchronises the stream or copies device
+ *     data to the host.
+ *   - Arguments are validated on the host before anything is enqueued. On any
+ *     negative status nothing has been enqueued and no output was touched.
+ *   - T = 0 is a no-op that returns COLI_OK.
+ *   - Faults inside kernels surface as HIP errors at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *
+ * Data layout (row-major throughout):
+ *   x            fp32 [T][H]
+ *   experts      (E + has_shared) expert blobs, blob i at experts + i * blob_bytes;
+ *                a blob is gate[F rows] | up[F rows] | down[H rows] of packed rows;
+ *                gate and up rows have H inputs, down rows have F inputs.
+ *                The shared expert, when present, is blob E.
+ *   scales       fp32 [(E + has_shared)][2F + H]: gate rows, up rows, down rows.
+ *   router_w     fp32 [E][H];  router_bias fp32 [E] (noaux_tc correction bias).
+ *   Packed row of n inputs = n/32 blocks of 32 values, two's complement:
+ *     int8 (wfmt 8): 32 bytes/block, byte i = value i;
+ *     int4 (wfmt 4): 16 bytes/block, byte j = value j | value (j+16) << 4;
+ *     int2 (wfmt 2):  8 bytes/block, byte j = sum_m value (j+8m) << 2m, m = 0..3.
+ *   Dequantised weight = scale[row] * value.
+ *
+ * Numerics (the readings):
+ *   Q8_0: per 32-value block d = max|x| / 127 (one fp32 division, stored fp32),
+ *     q = round-half-away-from-zero(x / d) clamped to [-127, 127]; d = 0 gives q = 0.
+ *   Router: z = x . W_e accumulated in fp64 from exact fp32 products,
+ *     s = 1 / (1 + exp(-z)) and c = s + bias in fp64; G contiguous groups of E/G
+ *     experts scored by the sum of their two largest c (their c when E/G = 1);
+ *     the Gk best groups kept; the k best c inside them are the route, in
+ *     descending order; every tie goes to the lower index;
+ *     w_j = (float)(s_j / sum_j s_j * rsf), the sum taken in slot order.
+ *   Expert (SwiGLU): g = s_gate * sum_b xd_b * I_b, u likewise with the up rows,
+ *     where I_b is the exact int32 dot of block b; h = silu(g) * u in fp32;
+ *     hq, hd = Q8_0(h); y = s_down * sum_b hd_b * I_b(hq, down row).
+ *   Combine: out_t = sum_j w_tj * y_{e_tj} (j = 0..k-1 in order) + y_shared, fp32,
+ *     no atomics: results are bitwise reproducible run to run.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COLI_OK = 0,
+  COLI_E_INVALID = -1,     /* a config value or argument is invalid (NULL, negative size, bad enum) */
+  COLI_E_UNSUPPORTED = -2, /* valid but outside this library's limits (see coli_moe_cfg) */
+  COLI_E_WORKSPACE = -3,   /* workspace NULL or smaller than coli_moe_workspace_bytes(cfg, T) */
+  COLI_E_ALIGN = -4,       /* a pointer is not aligned as documented */
+  COLI_E_DEVICE = -5       /* the HIP runtime rejected a launch */
+} coli_status;
+
+typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8 } coli_wfmt;
+
+/* Layer shape. Limits: hidden and ffn multiples of 128; 1 <= n_experts <= 1024;
+ * n_experts % n_group == 0; 1 <= topk_group <= n_group <= 64;
+ * 1 <= top_k <= min(64, topk_group * n_experts / n_group); has_shared 0 or 1;
+ * wfmt 2, 4 or 8. */
+typedef struct {
+  int32_t hidden;               /* H */
+  int32_t ffn;                  /* F, width of every expert (shared included) */
+  int32_t n_experts;            /* E routed experts */
+  int32_t top_k;                /* k */
+  int32_t n_group;              /* G */
+  int32_t topk_group;           /* Gk */
+  float routed_scaling_factor;  /* rsf */
+  int32_t has_shared;           /* 1: blob E is a shared expert applied to every token */
+  int32_t wfmt;                 /* coli_wfmt, one format for all experts of the layer */
+} coli_moe_cfg;
+
+/* Device weights of one layer. experts: 16-byte aligned; router_w: 16-byte aligned;
+ * scales, router_bias: 4-byte aligned. */
+typedef struct {
+  const void *experts;
+  const float *scales;
+  const float *router_w;
+  const float *router_bias;
+} coli_moe_weights;
+
+/* Bytes of one packed expert blob (0 if cfg is invalid). */
+size_t coli_moe_blob_bytes(const coli_moe_cfg *cfg);
+
+/* Workspace bytes that coli_moe_route / coli_moe_ffn / coli_moe_layer need for
+ * up to T_max tokens (0 if cfg is invalid or T_max out of range). T_max * top_k
+ * must not exceed 65535. The workspace must be 256-byte aligned. */
+size_t coli_moe_workspace_bytes(const coli_moe_cfg *cfg, int32_t T_max);
+
+/* Q8_0 quantisation of rows x cols fp32 values (cols % 32 == 0, x 16-byte aligned):
+ * q int8 [rows][cols] (4-byte aligned), d fp32 [rows][cols/32].
+ * Follows colibri-strix README, "What's implemented", integer-dot kernels item. */
+int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, void *stream);
+
+/* Sigmoid noaux_tc router for T tokens: topk_idx int32 [T][k] (expert ids, slot
+ * order), topk_w fp32 [T][k]. Uses the workspace for fp64 logits.
+ * Follows colibri-strix README, "What's implemented", router item. */
+int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                   int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream);
+
+/* Batch-union grouping of the T*k pairs p = t*k + j (no workspace):
+ *   expert_cnt int32 [E]: pairs per expert;
+ *   expert_off int32 [E+1]: exclusive prefix sum, expert_off[E] = T*k;
+ *   pair_perm int32 [T*k]: pair ids sorted by (expert, p) ascending;
+ *   active int32 [E]: experts with cnt > 0, ascending, in the first *n_active entries;
+ *   n_active int32 [1].
+ * topk_idx values must lie in [0, E) (checked by the kernel: out-of-range ids are
+ * counted nowhere and leave n_active = -1).
+ * Follows colibri-strix README, "What's implemented", batch-union item. */
+int coli_moe_group(const coli_moe_cfg *cfg, const int32_t *topk_idx, int32_t T, int32_t *expert_cnt,
+                   int32_t *expert_off, int32_t *pair_perm, int32_t *active, int32_t *n_active,
+                   void *stream);
+
+/* Expert FFNs over the batch union and the combine, given a route and its
+ * grouping (the outputs of coli_moe_route and coli_moe_group for the same T):
+ * quantises x (Q8_0), runs gate/up with fused SiLU*up and Q8_0 requantisation,
+ * runs down, then out fp32 [T][H] = slot-order weighted sum + shared expert.
+ * Follows the router, batch-union, quantization-kernel and integer-dot items of
+ * colibri-strix README, "What's implemented". */
+int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                 const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off,
+                 const int32_t *pair_perm, const int32_t *active, const int32_t *n_active, float *out,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/* The whole layer on one stream: route, group, FFN, combine. topk_idx_opt and
+ * topk_w_opt ([T][k]) receive the route when non-NULL. */
+int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                   int32_t *topk_idx_opt, float *topk_w_opt, void *workspace, size_t ws_bytes, void *stream);
+
+/* Measurement variant of coli_moe_layer: events[i] (hipEvent_t passed as void*,
+ * created by the caller) is recorded on `stream` just before stage i and
+ * events[n_stages] after the last stage; n_events must be coli_moe_num_stages()+1.
+ * Results are identical to coli_moe_layer. */
+int coli_moe_layer_profiled(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                            float *out, void *workspace, size_t ws_bytes, void *stream, void **events,
+                            int32_t n_events);
+int coli_moe_num_stages(void);
+const char *coli_moe_stage_name(int32_t stage);
+
+/* Static text for a status code. */
+const char *coli_moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,213 @@
+"""Python binding of libcolimoe.so: one routed MoE layer in HIP kernels for gfx950.
+
+Argument marshalling only. Every step of the layer runs in the library's kernels;
+PyTorch supplies device memory and the stream. There is no fallback path: if the
+library is not built, importing any entry point raises.
+
+Entry points (same names as the C ABI in include/coli_moe.h):
+    quantize_q8_0, route, group, ffn, layer, layer_profiled,
+    blob_bytes, workspace_bytes, num_stages, stage_name, strerror.
+Tensors must be CUDA tensors, contiguous, with the dtypes documented in the header.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcolimoe.so")
+
+COLI_OK, COLI_E_INVALID, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_ALIGN, COLI_E_DEVICE = 0, -1, -2, -3, -4, -5
+
+
+class ColiError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+
+
+class Cfg(C.Structure):
+    """coli_moe_cfg."""
+    _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("n_group", C.c_int32), ("topk_group", C.c_int32), ("routed_scaling_factor", C.c_float),
+                ("has_shared", C.c_int32), ("wfmt", C.c_int32)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [("experts", C.c_void_p), ("scales", C.c_void_p), ("router_w", C.c_void_p),
+                ("router_bias", C.c_void_p)]
+
+
+def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, has_shared=False, wbits=4,
+             **_ignored) -> Cfg:
+    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits)
+
+
+@dataclass
+class Weights:
+    """Device tensors of one layer: experts uint8 [(E+S) * blob], scales fp32 [(E+S), 2F+H],
+    router_w fp32 [E, H], router_bias fp32 [E]."""
+    experts: object
+    scales: object
+    router_w: object
+    router_bias: object
+
+    def c(self) -> _Weights:
+        return _Weights(_ptr(self.experts), _ptr(self.scales), _ptr(self.router_w), _ptr(self.router_bias))
+
+
+_lib = None
+
+EXPORTS = {
+    "coli_moe_blob_bytes": (C.c_size_t, [C.c_void_p]),
+    "coli_moe_workspace_bytes": (C.c_size_t, [C.c_void_p, C.c_int32]),
+    "coli_moe_quantize_q8_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "coli_moe_route": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_size_t, C.c_void_p]),
+    "coli_moe_group": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_void_p, C.c_void_p]),
+    "coli_moe_ffn": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                               C.c_size_t, C.c_void_p]),
+    "coli_moe_layer": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "coli_moe_layer_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                          C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p),
+                                          C.c_int32]),
+    "coli_moe_num_stages": (C.c_int, []),
+    "coli_moe_stage_name": (C.c_char_p, [C.c_int32]),
+    "coli_moe_strerror": (C.c_char_p, [C.c_int]),
+}
+
+
+def lib():
+    """Load libcolimoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(quantized_moe_sigmoid_amd/build.py); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, ref):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dt(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _check(rc, what):
+    if rc != COLI_OK:
+        raise ColiError(rc, what)
+
+
+def strerror(status: int) -> str:
+    return lib().coli_moe_strerror(status).decode()
+
+
+def blob_bytes(cfg: Cfg) -> int:
+    return int(lib().coli_moe_blob_bytes(C.byref(cfg)))
+
+
+def workspace_bytes(cfg: Cfg, T_max: int) -> int:
+    return int(lib().coli_moe_workspace_bytes(C.byref(cfg), T_max))
+
+
+def num_stages() -> int:
+    return int(lib().coli_moe_num_stages())
+
+
+def stage_name(i: int) -> str:
+    return lib().coli_moe_stage_name(i).decode()
+
+
+def alloc_workspace(cfg: Cfg, T_max: int, device="cuda"):
+    import torch
+    n = workspace_bytes(cfg, T_max)
+    if n == 0:
+        raise ColiError(COLI_E_UNSUPPORTED, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def quantize_q8_0(x, q, d, stream=None):
+    import torch
+    _dt(x, torch.float32, "x"), _dt(q, torch.int8, "q"), _dt(d, torch.float32, "d")
+    rows, cols = x.shape
+    _check(lib().coli_moe_quantize_q8_0(_ptr(x), rows, cols, _ptr(q), _ptr(d), _stream(stream, x)),
+           "coli_moe_quantize_q8_0")
+
+
+def route(cfg: Cfg, w: Weights, x, topk_idx, topk_w, workspace, stream=None):
+    import torch
+    _dt(x, torch.float32, "x"), _dt(topk_idx, torch.int32, "topk_idx"), _dt(topk_w, torch.float32, "topk_w")
+    wc = w.c()
+    _check(lib().coli_moe_route(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(topk_idx), _ptr(topk_w),
+                                _ptr(workspace), workspace.numel(), _stream(stream, x)), "coli_moe_route")
+
+
+def group(cfg: Cfg, topk_idx, T, cnt, off, perm, active, n_active, stream=None):
+    import torch
+    for n, t in (("topk_idx", topk_idx), ("cnt", cnt), ("off", off), ("perm", perm), ("active", active),
+                 ("n_active", n_active)):
+        _dt(t, torch.int32, n)
+    _check(lib().coli_moe_group(C.byref(cfg), _ptr(topk_idx), T, _ptr(cnt), _ptr(off), _ptr(perm), _ptr(active),
+                                _ptr(n_active), _stream(stream, topk_idx)), "coli_moe_group")
+
+
+def ffn(cfg: Cfg, w: Weights, x, topk_idx, topk_w, off, perm, active, n_active, out, workspace, stream=None):
+    import torch
+    _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out"), _dt(topk_w, torch.float32, "topk_w")
+    wc = w.c()
+    _check(lib().coli_moe_ffn(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(topk_idx), _ptr(topk_w),
+                              _ptr(off), _ptr(perm), _ptr(active), _ptr(n_active), _ptr(out), _ptr(workspace),
+                              workspace.numel(), _stream(stream, x)), "coli_moe_ffn")
+
+
+def layer(cfg: Cfg, w: Weights, x, out, workspace, topk_idx=None, topk_w=None, stream=None):
+    import torch
+    _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out")
+    if topk_idx is not None:
+        _dt(topk_idx, torch.int32, "topk_idx")
+    if topk_w is not None:
+        _dt(topk_w, torch.float32, "topk_w")
+    wc = w.c()
+    _check(lib().coli_moe_layer(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx),
+                                _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(stream, x)),
+           "coli_moe_layer")
+
+
+def layer_profiled(cfg: Cfg, w: Weights, x, out, workspace, events, stream=None):
+    """events: list of num_stages()+1 torch.cuda.Event(enable_timing=True)."""
+    import torch
+    _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out")
+    for e in events:  # torch creates the HIP event lazily, on its first record
+        if e.cuda_event == 0:
+            e.record(stream if stream is not None else torch.cuda.current_stream(x.device))
+    arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+    wc = w.c()
+    _check(lib().coli_moe_layer_profiled(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream, x), arr, len(events)),
+           "coli_moe_layer_profiled")

@@ -1,0 +1,57 @@
+// coli_internal.h — shared declarations of the HIP side of libcolimoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/coli_moe.h"
+
+namespace coli {
+
+constexpr int QK = 32;              // Q8_0 block length
+constexpr int WAVE = 64;            // CDNA wavefront
+constexpr int GEMV_ROWS = 32;       // rows per workgroup tile of the GEMV kernels (= one Q8_0 block of h)
+constexpr int GEMV_NT = 8;          // tokens handled per pass of the GEMV kernels
+constexpr int ROUTE_KC = 256;       // K chunk of the router logits kernel (decode tiling)
+
+// Packed bytes of one row of n inputs.
+__host__ __device__ inline int64_t row_bytes(int wfmt, int n) { return (int64_t)n * wfmt / 8; }
+
+struct WsLayout {
+  // byte offsets into the workspace (all 256-byte aligned)
+  size_t xq, xds, hq, hds, ypair, logits, idx, w, cnt, off, perm, active, nact, total;
+};
+
+// Workspace layout for T tokens (valid cfg assumed).
+WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit);
+
+// number of K splits of the router logits for T tokens
+int32_t route_ksplit(const coli_moe_cfg &c, int32_t T);
+
+// ---- launchers (host side, one per kernel family); return hipError_t
+hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, int2 *ds,
+                       hipStream_t s);
+hipError_t launch_route(const coli_moe_cfg &c, const float *x, int32_t T, const float *W, const float *bias,
+                        double *logits, int32_t ksplit, int32_t *idx, float *w, hipStream_t s, hipEvent_t mid);
+hipError_t launch_group(const coli_moe_cfg &c, const int32_t *idx, int32_t T, int32_t *cnt, int32_t *off,
+                        int32_t *perm, int32_t *active, int32_t *nact, hipStream_t s);
+
+struct FfnArgs {
+  const uint8_t *experts;
+  const float *scales;
+  int64_t blob_bytes;
+  int32_t H, F, E, k, T, has_shared;
+  const int32_t *off, *perm, *active, *nact;
+  const int8_t *xq;   // [T][H]
+  const int2 *xds;    // [T][H/32] {d bits, block sum}
+  int8_t *hq;         // [P+T][F]
+  int2 *hds;          // [P+T][F/32]
+  float *ypair;       // [P+T][H]
+};
+hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s);
+hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s);
+hipError_t launch_combine(const float *ypair, const float *w, int32_t T, int32_t k, int32_t H,
+                          int32_t has_shared, float *out, hipStream_t s);
+
+}  // namespace coli

@@ -1,0 +1,275 @@
+// coli_moe_api.hip — the C ABI of libcolimoe: host-side validation, workspace
+// layout and the launch sequence of the routed MoE layer (one stream, no host
+// synchronisation, no device allocation).
+#include <limits.h>
+
+#include "coli_internal.h"
+
+namespace coli {
+bool group_supported(int P, int E);
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit) {
+  const size_t H = c.hidden, F = c.ffn, E = c.n_experts, k = c.top_k;
+  const size_t P = (size_t)T * k, R = P + (size_t)T * c.has_shared;  // pair rows (+ shared rows)
+  WsLayout L{};
+  size_t o = 0;
+  L.xq = o;     o = align256(o + (size_t)T * H);
+  L.xds = o;    o = align256(o + (size_t)T * (H / QK) * sizeof(int2));
+  L.hq = o;     o = align256(o + R * F);
+  L.hds = o;    o = align256(o + R * (F / QK) * sizeof(int2));
+  L.ypair = o;  o = align256(o + R * H * sizeof(float));
+  L.logits = o; o = align256(o + (size_t)ksplit * T * E * sizeof(double));
+  L.idx = o;    o = align256(o + P * sizeof(int32_t));
+  L.w = o;      o = align256(o + P * sizeof(float));
+  L.cnt = o;    o = align256(o + E * sizeof(int32_t));
+  L.off = o;    o = align256(o + (E + 1) * sizeof(int32_t));
+  L.perm = o;   o = align256(o + P * sizeof(int32_t));
+  L.active = o; o = align256(o + E * sizeof(int32_t));
+  L.nact = o;   o = align256(o + sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+static constexpr size_t GEMV_LDS_LIMIT = 64 * 1024;
+
+static size_t gemv_lds(int K) {
+  return (size_t)GEMV_NT * K + (size_t)GEMV_NT * (K / QK) * sizeof(int2) + (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) +
+         2 * GEMV_NT * sizeof(int);
+}
+
+static int check_cfg(const coli_moe_cfg *c) {
+  if (!c) return COLI_E_INVALID;
+  if (c->hidden <= 0 || c->ffn <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->n_group <= 0 ||
+      c->topk_group <= 0)
+    return COLI_E_INVALID;
+  if (c->wfmt != 2 && c->wfmt != 4 && c->wfmt != 8) return COLI_E_INVALID;
+  if (c->has_shared != 0 && c->has_shared != 1) return COLI_E_INVALID;
+  if (c->n_experts % c->n_group || c->topk_group > c->n_group) return COLI_E_INVALID;
+  if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return COLI_E_INVALID;
+  if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return COLI_E_INVALID;  // NaN
+  if (c->hidden % 128 || c->ffn % 128) return COLI_E_UNSUPPORTED;
+  if (c->n_experts > 1024 || c->n_group > 64 || c->top_k > 64) return COLI_E_UNSUPPORTED;
+  if (gemv_lds(c->hidden) > GEMV_LDS_LIMIT || gemv_lds(c->ffn) > GEMV_LDS_LIMIT) return COLI_E_UNSUPPORTED;
+  if ((int64_t)c->hidden * c->ffn > ((int64_t)1 << 40)) return COLI_E_UNSUPPORTED;
+  return COLI_OK;
+}
+
+static int check_T(const coli_moe_cfg *c, int32_t T) {
+  if (T < 0) return COLI_E_INVALID;
+  if ((int64_t)T * c->top_k > 65535) return COLI_E_UNSUPPORTED;
+  if (T > 0 && !group_supported(T * c->top_k, c->n_experts)) return COLI_E_UNSUPPORTED;
+  return COLI_OK;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_weights(const coli_moe_weights *w, bool need_experts, bool need_router) {
+  if (!w) return COLI_E_INVALID;
+  if (need_experts) {
+    if (!w->experts || !w->scales) return COLI_E_INVALID;
+    if (!aligned(w->experts, 16) || !aligned(w->scales, 4)) return COLI_E_ALIGN;
+  }
+  if (need_router) {
+    if (!w->router_w || !w->router_bias) return COLI_E_INVALID;
+    if (!aligned(w->router_w, 16) || !aligned(w->router_bias, 4)) return COLI_E_ALIGN;
+  }
+  return COLI_OK;
+}
+
+static int dev(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_DEVICE; }
+
+template <typename Tp>
+static Tp *at(void *ws, size_t off) {
+  return reinterpret_cast<Tp *>(static_cast<char *>(ws) + off);
+}
+
+static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const float *x, int32_t T,
+                       const float *topk_w, const int32_t *off, const int32_t *perm, const int32_t *active,
+                       const int32_t *nact, float *out, void *ws, const WsLayout &L, hipStream_t s,
+                       hipEvent_t *ev) {
+  int st;
+  if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
+  if ((st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), nullptr, at<int2>(ws, L.xds), s)))) return st;
+  FfnArgs a{};
+  a.experts = static_cast<const uint8_t *>(w.experts);
+  a.scales = w.scales;
+  a.blob_bytes = coli_moe_blob_bytes(&c);
+  a.H = c.hidden;
+  a.F = c.ffn;
+  a.E = c.n_experts;
+  a.k = c.top_k;
+  a.T = T;
+  a.has_shared = c.has_shared;
+  a.off = off;
+  a.perm = perm;
+  a.active = active;
+  a.nact = nact;
+  a.xq = at<int8_t>(ws, L.xq);
+  a.xds = at<int2>(ws, L.xds);
+  a.hq = at<int8_t>(ws, L.hq);
+  a.hds = at<int2>(ws, L.hds);
+  a.ypair = at<float>(ws, L.ypair);
+  if (ev && (st = dev(hipEventRecord(ev[1], s)))) return st;
+  if ((st = dev(launch_gateup(c.wfmt, a, s)))) return st;
+  if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
+  if ((st = dev(launch_down(c.wfmt, a, s)))) return st;
+  if (ev && (st = dev(hipEventRecord(ev[3], s)))) return st;
+  if ((st = dev(launch_combine(a.ypair, topk_w, T, c.top_k, c.hidden, c.has_shared, out, s)))) return st;
+  if (ev && (st = dev(hipEventRecord(ev[4], s)))) return st;
+  return COLI_OK;
+}
+
+// stage order of coli_moe_layer_profiled
+static const char *const kStages[] = {"route_logits", "route_topk", "group", "quantize_x",
+                                      "ffn_gate_up", "ffn_down", "combine"};
+static constexpr int kNumStages = 7;
+
+static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                      int32_t *idx_opt, float *w_opt, void *ws, size_t ws_bytes, void *stream, hipEvent_t *ev) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if ((st = check_weights(w, true, true))) return st;
+  if (!x || !out) return COLI_E_INVALID;
+  if (!aligned(x, 16) || !aligned(out, 16)) return COLI_E_ALIGN;
+  if ((idx_opt && !aligned(idx_opt, 4)) || (w_opt && !aligned(w_opt, 4))) return COLI_E_ALIGN;
+  const int32_t ks = route_ksplit(*cfg, T);
+  const WsLayout L = ws_layout(*cfg, T, ks);
+  if (!ws || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  if (!aligned(ws, 256)) return COLI_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t *idx = idx_opt ? idx_opt : at<int32_t>(ws, L.idx);
+  float *tw = w_opt ? w_opt : at<float>(ws, L.w);
+  if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
+  if ((st = dev(launch_route(*cfg, x, T, w->router_w, w->router_bias, at<double>(ws, L.logits), ks, idx, tw, s,
+                             ev ? ev[1] : nullptr))))
+    return st;
+  if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
+  int32_t *off = at<int32_t>(ws, L.off), *perm = at<int32_t>(ws, L.perm), *act = at<int32_t>(ws, L.active),
+          *nact = at<int32_t>(ws, L.nact);
+  if ((st = dev(launch_group(*cfg, idx, T, at<int32_t>(ws, L.cnt), off, perm, act, nact, s)))) return st;
+  return ffn_enqueue(*cfg, *w, x, T, tw, off, perm, act, nact, out, ws, L, s, ev ? ev + 3 : nullptr);
+}
+
+}  // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+size_t coli_moe_blob_bytes(const coli_moe_cfg *cfg) {
+  if (check_cfg(cfg) != COLI_OK) return 0;
+  return (size_t)(2 * (int64_t)cfg->ffn * row_bytes(cfg->wfmt, cfg->hidden) +
+                  (int64_t)cfg->hidden * row_bytes(cfg->wfmt, cfg->ffn));
+}
+
+size_t coli_moe_workspace_bytes(const coli_moe_cfg *cfg, int32_t T_max) {
+  if (check_cfg(cfg) != COLI_OK || check_T(cfg, T_max) != COLI_OK) return 0;
+  // the K split of the router depends on T: take the largest over T <= T_max
+  size_t best = 0;
+  const int32_t cand[2] = {T_max < 16 ? T_max : 16, T_max};
+  for (int i = 0; i < 2; i++) {
+    const WsLayout L = ws_layout(*cfg, T_max, route_ksplit(*cfg, cand[i]));
+    if (L.total > best) best = L.total;
+  }
+  return best;
+}
+
+int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, void *stream) {
+  if (rows < 0 || cols <= 0) return COLI_E_INVALID;
+  if (cols % QK) return COLI_E_UNSUPPORTED;
+  if (rows == 0) return COLI_OK;
+  if (!x || !q || !d) return COLI_E_INVALID;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4)) return COLI_E_ALIGN;
+  return dev(launch_q8_0(x, rows, cols, q, d, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                   int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if ((st = check_weights(w, false, true))) return st;
+  if (!x || !topk_idx || !topk_w) return COLI_E_INVALID;
+  if (!aligned(x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return COLI_E_ALIGN;
+  const int32_t ks = route_ksplit(*cfg, T);
+  const WsLayout L = ws_layout(*cfg, T, ks);
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return COLI_E_ALIGN;
+  return dev(launch_route(*cfg, x, T, w->router_w, w->router_bias, at<double>(workspace, L.logits), ks, topk_idx,
+                          topk_w, static_cast<hipStream_t>(stream), nullptr));
+}
+
+int coli_moe_group(const coli_moe_cfg *cfg, const int32_t *topk_idx, int32_t T, int32_t *expert_cnt,
+                   int32_t *expert_off, int32_t *pair_perm, int32_t *active, int32_t *n_active, void *stream) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if (!topk_idx || !expert_cnt || !expert_off || !pair_perm || !active || !n_active) return COLI_E_INVALID;
+  if (!aligned(topk_idx, 4) || !aligned(expert_cnt, 4) || !aligned(expert_off, 4) || !aligned(pair_perm, 4) ||
+      !aligned(active, 4) || !aligned(n_active, 4))
+    return COLI_E_ALIGN;
+  return dev(launch_group(*cfg, topk_idx, T, expert_cnt, expert_off, pair_perm, active, n_active,
+                          static_cast<hipStream_t>(stream)));
+}
+
+int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                 const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm,
+                 const int32_t *active, const int32_t *n_active, float *out, void *workspace, size_t ws_bytes,
+                 void *stream) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if ((st = check_weights(w, true, false))) return st;
+  if (!x || !topk_idx || !topk_w || !expert_off || !pair_perm || !active || !n_active || !out)
+    return COLI_E_INVALID;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||
+      !aligned(pair_perm, 4) || !aligned(active, 4) || !aligned(n_active, 4))
+    return COLI_E_ALIGN;
+  const WsLayout L = ws_layout(*cfg, T, route_ksplit(*cfg, T));
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return COLI_E_ALIGN;
+  return ffn_enqueue(*cfg, *w, x, T, topk_w, expert_off, pair_perm, active, n_active, out, workspace, L,
+                     static_cast<hipStream_t>(stream), nullptr);
+}
+
+int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                   int32_t *topk_idx_opt, float *topk_w_opt, void *workspace, size_t ws_bytes, void *stream) {
+  return layer_impl(cfg, w, x, T, out, topk_idx_opt, topk_w_opt, workspace, ws_bytes, stream, nullptr);
+}
+
+int coli_moe_layer_profiled(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                            float *out, void *workspace, size_t ws_bytes, void *stream, void **events,
+                            int32_t n_events) {
+  if (!events || n_events != kNumStages + 1) return COLI_E_INVALID;
+  for (int i = 0; i < n_events; i++)
+    if (!events[i]) return COLI_E_INVALID;
+  return layer_impl(cfg, w, x, T, out, nullptr, nullptr, workspace, ws_bytes, stream,
+                    reinterpret_cast<hipEvent_t *>(events));
+}
+
+int coli_moe_num_stages(void) { return kNumStages; }
+
+const char *coli_moe_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < kNumStages) ? kStages[stage] : "";
+}
+
+const char *coli_moe_strerror(int status) {
+  switch (status) {
+    case COLI_OK: return "ok";
+    case COLI_E_INVALID: return "invalid argument or configuration";
+    case COLI_E_UNSUPPORTED: return "configuration outside the library's limits";
+    case COLI_E_WORKSPACE: return "workspace missing or too small";
+    case COLI_E_ALIGN: return "pointer not aligned as required";
+    case COLI_E_DEVICE: return "HIP runtime rejected a launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,383 @@
+// ffn_gemv.hip — quantised expert GEMV over the batch union, gfx950.
+//
+// One expert of the union is one grid row (blockIdx.y = slot); a workgroup owns
+// 32 consecutive output rows of that expert and streams their packed weights
+// exactly once, applying them to every token routed to the expert (batch-union:
+// colibri-strix README, "What's implemented", batch-union item). Weights stay
+// packed in HBM and are dequantised on use (same section, quantization kernels
+// item); the products are integer dots against Q8_0 activations (integer-dot
+// kernels item):
+//   I_b = sum over block b of xq * wq         (v_dot4_i32_i8, exact int32)
+//   acc = sum_b d_b * I_b                     (fp32)
+//   out = s_row * acc
+// Packed int4 / int2 fields are two's complement; XOR with 0x88.. / 0xAA.. turns
+// them into offset-binary u = w + 8 / w + 2 (0..15 / 0..3), so a plain signed
+// dot4 applies and I_b = dot(xq, u) - 8 * sum(xq) (resp. 2 * sum), with the
+// block sum of xq precomputed next to its scale.
+//
+// Lane mapping: the 16-byte "chunk" of a packed row is one Q8_0 block for int4,
+// half of one for int8 (the two halves go to one lane as a 32-byte chunk) and
+// two blocks for int2. LPR lanes share one row (each loads every LPR-th chunk),
+// so one load instruction of a wavefront covers 64 consecutive chunks of one
+// row (LPR = 64) or of 64/LPR rows: fully coalesced 128-bit weight loads.
+// Activations of up to GEMV_NT tokens are staged in LDS once per workgroup.
+//
+// Gate/up epilogue (fused): h = silu(g) * u in fp32, then Q8_0 of the 32 rows of
+// the tile (one block of h per token): hq int8 and {hd, sum hq}.
+// Down epilogue: y fp32 rows, written per token as 32 consecutive floats.
+#include "coli_internal.h"
+
+namespace coli {
+
+template <int WB>
+struct Fmt;
+template <>
+struct Fmt<4> {
+  static constexpr int CHUNK = 16;  // bytes per lane chunk
+  static constexpr int BPC = 1;     // Q8_0 blocks per chunk
+};
+template <>
+struct Fmt<8> {
+  static constexpr int CHUNK = 32;
+  static constexpr int BPC = 1;
+};
+template <>
+struct Fmt<2> {
+  static constexpr int CHUNK = 16;
+  static constexpr int BPC = 2;
+};
+
+__device__ __forceinline__ int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+// Integer dot of one weight chunk with the activation block(s) it covers, times
+// the activation block scale(s); returns the fp32 contribution.
+template <int WB>
+__device__ __forceinline__ float chunk_dot(const uint32_t (&wq)[Fmt<WB>::CHUNK / 4], const int8_t *xa,
+                                           const int2 *xds);
+
+template <>
+__device__ __forceinline__ float chunk_dot<4>(const uint32_t (&wq)[4], const int8_t *xa, const int2 *xds) {
+  const int4 xl = *reinterpret_cast<const int4 *>(xa);
+  const int4 xh = *reinterpret_cast<const int4 *>(xa + 16);
+  const int2 ds = xds[0];
+  const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+  int acc = -8 * ds.y;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t t = wq[i] ^ 0x88888888u;
+    acc = dot4((int)(t & 0x0F0F0F0Fu), xv[i], acc);
+    acc = dot4((int)((t >> 4) & 0x0F0F0F0Fu), xv[4 + i], acc);
+  }
+  return __int_as_float(ds.x) * (float)acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<8>(const uint32_t (&wq)[8], const int8_t *xa, const int2 *xds) {
+  const int4 xl = *reinterpret_cast<const int4 *>(xa);
+  const int4 xh = *reinterpret_cast<const int4 *>(xa + 16);
+  const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+  int acc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc = dot4((int)wq[i], xv[i], acc);
+  return __int_as_float(xds[0].x) * (float)acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<2>(const uint32_t (&wq)[4], const int8_t *xa, const int2 *xds) {
+  float r = 0.0f;
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++) {
+    const int4 xl = *reinterpret_cast<const int4 *>(xa + 32 * blk);
+    const int4 xh = *reinterpret_cast<const int4 *>(xa + 32 * blk + 16);
+    const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+    const int2 ds = xds[blk];
+    int acc = -2 * ds.y;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint32_t t = wq[2 * blk + h] ^ 0xAAAAAAAAu;
+#pragma unroll
+      for (int m = 0; m < 4; m++) acc = dot4((int)((t >> (2 * m)) & 0x03030303u), xv[2 * m + h], acc);
+    }
+    r += __int_as_float(ds.x) * (float)acc;
+  }
+  return r;
+}
+
+template <int WB>
+__device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<WB>::CHUNK / 4]) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(p);
+  wq[0] = a.x;
+  wq[1] = a.y;
+  wq[2] = a.z;
+  wq[3] = a.w;
+  if constexpr (Fmt<WB>::CHUNK == 32) {
+    const uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
+    wq[4] = b.x;
+    wq[5] = b.y;
+    wq[6] = b.z;
+    wq[7] = b.w;
+  }
+}
+
+enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+
+// Resolve a grid slot to (expert, number of tokens, segment start). Returns false
+// if the slot has no work. Slot 0 is the shared expert when there is one.
+__device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, int &e, int &n, int &beg, bool &shared) {
+  if (a.has_shared && slot == 0) {
+    e = a.E;
+    n = a.T;
+    beg = 0;
+    shared = true;
+    return n > 0;
+  }
+  const int u = slot - a.has_shared;
+  const int na = *a.nact;
+  if (u >= na) return false;
+  e = a.active[u];
+  beg = a.off[e];
+  n = a.off[e + 1] - beg;
+  shared = false;
+  return n > 0;
+}
+
+template <int WB, int LPR, int MODE>
+__global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
+  constexpr int NT = GEMV_NT;
+  constexpr int RPI = WAVE / LPR;        // rows per wave iteration
+  constexpr int WROWS = GEMV_ROWS / 4;   // rows per wave
+  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int CW = Fmt<WB>::CHUNK / 4;
+  constexpr int BPC = Fmt<WB>::BPC;
+
+  int e, n, beg;
+  bool shared;
+  if (!resolve_slot(a, blockIdx.y, e, n, beg, shared)) return;
+
+  const int K = (MODE == MODE_GATEUP) ? a.H : a.F;       // inputs per row
+  const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;   // output rows per matrix
+  const int nkb = K / QK;
+  const int nchunk = nkb / BPC;
+  const int cpl = nchunk / LPR;
+  const int64_t rb = row_bytes(WB, K);
+  const int P = a.T * a.k;
+
+  const uint8_t *blob = a.experts + (int64_t)e * a.blob_bytes;
+  const int64_t rbh = row_bytes(WB, a.H);
+  const uint8_t *mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+  const uint8_t *mat1 = blob + (int64_t)a.F * rbh;  // up (gate/up mode only)
+  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  const float *sc0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * a.F;
+  const float *sc1 = sc + a.F;
+
+  extern __shared__ __align__(16) char smem[];
+  int8_t *xs = reinterpret_cast<int8_t *>(smem);                      // [NT][K]
+  int2 *xds = reinterpret_cast<int2 *>(smem + NT * K);                // [NT][nkb]
+  float *obuf = reinterpret_cast<float *>(xds + NT * nkb);            // [NT][32]
+  int *orow = reinterpret_cast<int *>(obuf + NT * GEMV_ROWS);         // [NT]
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rs = lane / LPR, sub = lane % LPR;
+  const int r0 = blockIdx.x * GEMV_ROWS;
+
+  for (int tc = 0; tc < n; tc += NT) {
+    const int nt = min(NT, n - tc);
+    // token -> activation row and output row
+    if (tid < NT) {
+      int out = -1, act = 0;
+      if (tid < nt) {
+        const int i = tc + tid;
+        out = shared ? P + i : a.perm[beg + i];
+        act = (MODE == MODE_GATEUP) ? (shared ? i : out / a.k) : out;
+      }
+      orow[tid] = out;
+      orow[NT + tid] = act;
+    }
+    __syncthreads();
+    // stage activations (16 bytes per thread per step) and their block scales
+    const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
+    const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+    const int v16 = K / 16;
+    for (int i = tid; i < nt * v16; i += 256) {
+      const int t = i / v16, c = i % v16;
+      const int act = orow[NT + t];
+      *reinterpret_cast<int4 *>(xs + t * K + c * 16) =
+          *reinterpret_cast<const int4 *>(asrc + (int64_t)act * K + c * 16);
+    }
+    for (int i = tid; i < nt * nkb; i += 256) {
+      const int t = i / nkb, b = i % nkb;
+      xds[t * nkb + b] = dsrc[(int64_t)orow[NT + t] * nkb + b];
+    }
+    __syncthreads();
+
+    for (int it = 0; it < WROWS; it += RPI) {
+      const int rl = it + rs;  // row within this wave's WROWS
+      const bool rv = rl < WROWS;
+      const int r = r0 + wv * WROWS + (rv ? rl : 0);
+      const uint8_t *p0 = mat0 + (int64_t)r * rb;
+      const uint8_t *p1 = mat1 + (int64_t)r * rb;
+      float acc0[NT], acc1[NT];
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        acc0[t] = 0.0f;
+        acc1[t] = 0.0f;
+      }
+      for (int ci = 0; ci < cpl; ci++) {
+        const int c = sub + ci * LPR;
+        uint32_t w0[CW], w1[CW];
+        load_chunk<WB>(p0 + (int64_t)c * Fmt<WB>::CHUNK, w0);
+        if constexpr (NMAT == 2) load_chunk<WB>(p1 + (int64_t)c * Fmt<WB>::CHUNK, w1);
+        const int kx = c * BPC * QK;  // first input of this chunk
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          if (t < nt) {
+            const int8_t *xa = xs + t * K + kx;
+            const int2 *xd = xds + t * nkb + c * BPC;
+            acc0[t] += chunk_dot<WB>(w0, xa, xd);
+            if constexpr (NMAT == 2) acc1[t] += chunk_dot<WB>(w1, xa, xd);
+          }
+        }
+      }
+      // reduce across the LPR lanes of the row
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) {
+          acc0[t] += __shfl_xor(acc0[t], o);
+          if constexpr (NMAT == 2) acc1[t] += __shfl_xor(acc1[t], o);
+        }
+      }
+      if (rv && sub == 0) {
+        const int rloc = wv * WROWS + rl;
+        const float s0 = sc0[r];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          if (t < nt) {
+            float v;
+            if constexpr (MODE == MODE_GATEUP) {
+              const float g = s0 * acc0[t];
+              const float u = sc1[r] * acc1[t];
+              v = (g / (1.0f + expf(-g))) * u;
+            } else {
+              v = s0 * acc0[t];
+            }
+            obuf[t * GEMV_ROWS + rloc] = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // epilogue: 32 rows x nt tokens; half a wavefront per token
+    {
+      const int t = tid >> 5, i = tid & 31;
+      if (t < nt) {
+        const float v = obuf[t * GEMV_ROWS + i];
+        const int out = orow[t];
+        if constexpr (MODE == MODE_GATEUP) {
+          float am = fabsf(v);
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+          const float d = am / 127.0f;
+          int q = 0;
+          if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
+          int sum = q;
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+          a.hq[(int64_t)out * a.F + r0 + i] = (int8_t)q;
+          if (i == 0) a.hds[(int64_t)out * (a.F / QK) + r0 / QK] = make_int2(__float_as_int(d), sum);
+        } else {
+          a.ypair[(int64_t)out * a.H + r0 + i] = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// lanes per row: largest power of two <= 64 dividing the chunks per row
+static int pick_lpr(int nchunk) {
+  int l = 64;
+  while (l > 1 && nchunk % l) l >>= 1;
+  return l;
+}
+
+template <int WB, int MODE>
+static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
+  const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
+  const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;
+  const int nkb = K / QK;
+  const int nchunk = nkb / Fmt<WB>::BPC;
+  const int lpr = pick_lpr(nchunk);
+  const int slots = a.has_shared + min(a.E, a.T * a.k);
+  dim3 grid(NROWS / GEMV_ROWS, slots);
+  const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(int2) +
+                     (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
+  switch (lpr) {
+#define COLI_LPR_CASE(L) \
+  case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE>), grid, dim3(256), lds, s, a); break;
+    COLI_LPR_CASE(64)
+    COLI_LPR_CASE(32)
+    COLI_LPR_CASE(16)
+    COLI_LPR_CASE(8)
+    COLI_LPR_CASE(4)
+    COLI_LPR_CASE(2)
+    COLI_LPR_CASE(1)
+#undef COLI_LPR_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s) {
+  switch (wfmt) {
+    case 4: return launch_mode<4, MODE_GATEUP>(a, s);
+    case 8: return launch_mode<8, MODE_GATEUP>(a, s);
+    case 2: return launch_mode<2, MODE_GATEUP>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s) {
+  switch (wfmt) {
+    case 4: return launch_mode<4, MODE_DOWN>(a, s);
+    case 8: return launch_mode<8, MODE_DOWN>(a, s);
+    case 2: return launch_mode<2, MODE_DOWN>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// out[t] = sum_j w[t][j] * ypair[t*k + j] (j ascending) + ypair[P + t] (shared)
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ypair, const float *__restrict__ w,
+                                                      int T, int k, int H, int has_shared,
+                                                      float *__restrict__ out) {
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * 256 + threadIdx.x;  // float4 column
+  if (c4 * 4 >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; j++) {
+    const float wj = w[(int64_t)t * k + j];
+    const float4 y = reinterpret_cast<const float4 *>(ypair + ((int64_t)t * k + j) * H)[c4];
+    acc.x += wj * y.x;
+    acc.y += wj * y.y;
+    acc.z += wj * y.z;
+    acc.w += wj * y.w;
+  }
+  if (has_shared) {
+    const float4 y = reinterpret_cast<const float4 *>(ypair + ((int64_t)T * k + t) * H)[c4];
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  reinterpret_cast<float4 *>(out + (int64_t)t * H)[c4] = acc;
+}
+
+hipError_t launch_combine(const float *ypair, const float *w, int32_t T, int32_t k, int32_t H, int32_t has_shared,
+                          float *out, hipStream_t s) {
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, ypair, w, T, k, H, has_shared, out);
+  return hipGetLastError();
+}
+
+}  // namespace coli

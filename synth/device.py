@@ -1,0 +1,56 @@
+"""Device-side fill of synthetic expert blobs (libcolisynth.so), identical to
+synth.expert_blob() byte for byte. Used for workloads too large to generate on
+the host; the CPU side regenerates any single expert with synth.expert_blob()."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcolisynth.so")
+
+
+def build() -> str:
+    tmp = LIB_PATH + ".tmp"
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", os.path.join(HERE, "gen_device.hip"), "-o", tmp], check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        L.coli_synth_fill_blobs.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]
+        L.coli_synth_fill_blobs.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def fill_blobs(out, seed: int, layer: int, first_expert: int, n_blobs: int, blob_bytes: int, wbits: int):
+    """Fill the uint8 CUDA tensor ``out`` ([n_blobs * blob_bytes]) with blobs of experts
+    first_expert .. first_expert + n_blobs - 1 of (seed, layer)."""
+    import torch
+
+    assert out.is_cuda and out.dtype == torch.uint8 and out.is_contiguous()
+    assert out.numel() >= n_blobs * blob_bytes
+    keys = np.array([synth.derive_key(seed, synth.TAG_BLOB, layer, first_expert + i) for i in range(n_blobs)],
+                    dtype=np.uint64)
+    kd = torch.from_numpy(keys.view(np.int64)).to(out.device)
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    rc = lib().coli_synth_fill_blobs(C.c_void_p(out.data_ptr()), C.c_void_p(kd.data_ptr()), blob_bytes, n_blobs,
+                                     wbits, C.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"coli_synth_fill_blobs failed: {rc}")
+    torch.cuda.current_stream(out.device).synchronize()  # keys tensor lifetime

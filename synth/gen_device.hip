@@ -1,0 +1,53 @@
+// gen_device.hip — device-side twin of synth.expert_blob(): fills packed expert
+// blobs with the SplitMix64 stream of each expert's key. Integer arithmetic only,
+// so the bytes equal the host generator's bit for bit. Not part of the MoE
+// library: it only produces synthetic inputs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// byte b -> ((b * 255) >> 8) - 127 in each of the 8 bytes of v
+__device__ __forceinline__ uint64_t to_int8_weights(uint64_t v) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t b = (uint32_t)(v >> (8 * i)) & 0xFFu;
+    const int32_t q = (int32_t)((b * 255u) >> 8) - 127;
+    r |= (uint64_t)(uint8_t)(int8_t)q << (8 * i);
+  }
+  return r;
+}
+
+__global__ void fill_blobs_kernel(uint64_t *__restrict__ out, const uint64_t *__restrict__ keys, int64_t words_per_blob,
+                                  int32_t n_blobs, int32_t int8_map) {
+  const int64_t total = words_per_blob * n_blobs;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = g / words_per_blob, i = g % words_per_blob;
+    uint64_t v = mix64(keys[e] + (uint64_t)(i + 1) * kGolden);
+    if (int8_map) v = to_int8_weights(v);
+    out[g] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" int coli_synth_fill_blobs(void *out, const void *keys_dev, int64_t blob_bytes, int32_t n_blobs,
+                                     int32_t wbits, void *stream) {
+  if (!out || !keys_dev || blob_bytes <= 0 || blob_bytes % 8 || n_blobs <= 0) return -1;
+  if (((uintptr_t)out % 8) != 0) return -4;
+  const int64_t words = blob_bytes / 8;
+  hipLaunchKernelGGL(fill_blobs_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint64_t *>(out), static_cast<const uint64_t *>(keys_dev), words, n_blobs,
+                     wbits == 8 ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad calls on the
+host before anything is enqueued (CPU only: no call here reaches a kernel)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(coli_moe_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_moe_sigmoid_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        from quantized_moe_sigmoid_amd import build
+        build.build()
+    return q
+
+
+def test_exports_every_declared_symbol(q):
+    names = _declared()
+    assert "coli_moe_layer" in names and "coli_moe_route" in names
+    L = q.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(q.EXPORTS) == set(names)
+
+
+def test_host_queries(q):
+    c = q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 4)
+    assert q.blob_bytes(c) == 2 * 2048 * 3072 + 6144 * 1024
+    assert q.blob_bytes(q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 8)) == 3 * 2048 * 6144
+    assert q.blob_bytes(q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 2)) == 3 * 2048 * 6144 // 4
+    assert q.workspace_bytes(c, 16) > 0 and q.workspace_bytes(c, 2048) > q.workspace_bytes(c, 16)
+    assert q.num_stages() == 7
+    assert [q.stage_name(i) for i in range(7)][4] == "ffn_gate_up"
+    assert q.stage_name(99) == ""
+    for s in (0, -1, -2, -3, -4, -5):
+        assert q.strerror(s)
+    assert q.strerror(-77) == "unknown status"
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def _w(q, experts=FAKE, scales=FAKE, rw=FAKE, rb=FAKE):
+    return q._Weights(C.c_void_p(experts), C.c_void_p(scales), C.c_void_p(rw), C.c_void_p(rb))
+
+
+BAD_CFGS = [
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, n_group=3, topk_group=1), -1),   # E % G
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, n_group=2, topk_group=3), -1),   # Gk > G
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=9, n_group=2, topk_group=1), -1),   # k > Gk*E/G
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=0), -1),
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, wbits=3), -1),
+    (dict(hidden=160, ffn=128, n_experts=16, top_k=4), -2),                            # H % 128
+    (dict(hidden=256, ffn=96, n_experts=16, top_k=4), -2),                             # F % 128
+    (dict(hidden=256, ffn=128, n_experts=2048, top_k=4), -2),                          # E > 1024
+    (dict(hidden=16384, ffn=128, n_experts=16, top_k=4), -2),                          # LDS of the GEMV
+]
+
+
+@pytest.mark.parametrize("cfgd,want", BAD_CFGS)
+def test_bad_config_rejected(q, cfgd, want):
+    c = q.make_cfg(**cfgd)
+    L = q.lib()
+    w = _w(q)
+    p = C.c_void_p(FAKE)
+    assert L.coli_moe_blob_bytes(C.byref(c)) == 0
+    assert L.coli_moe_workspace_bytes(C.byref(c), 8) == 0
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 8, p, None, None, p, 1 << 30, None) == want
+    assert L.coli_moe_route(C.byref(c), C.byref(w), p, 8, p, p, p, 1 << 30, None) == want
+    assert L.coli_moe_group(C.byref(c), p, 8, p, p, p, p, p, None) == want
+    assert L.coli_moe_ffn(C.byref(c), C.byref(w), p, 8, p, p, p, p, p, p, p, p, 1 << 30, None) == want
+
+
+def test_argument_errors(q):
+    c = q.make_cfg(256, 128, 16, 4)
+    L = q.lib()
+    p = C.c_void_p(FAKE)
+    ws_need = L.coli_moe_workspace_bytes(C.byref(c), 8)
+    assert ws_need > 0
+    w = _w(q)
+    # T = 0 is a no-op
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), None, 0, None, None, None, None, 0, None) == 0
+    # negative T, T*k too large
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, -1, p, None, None, p, ws_need, None) == -1
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 20000, p, None, None, p, 1 << 40, None) == -2
+    assert L.coli_moe_workspace_bytes(C.byref(c), 20000) == 0
+    # NULL pointers
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), None, 8, p, None, None, p, ws_need, None) == -1
+    assert L.coli_moe_layer(C.byref(c), C.byref(_w(q, experts=0)), p, 8, p, None, None, p, ws_need, None) == -1
+    assert L.coli_moe_layer(C.byref(c), None, p, 8, p, None, None, p, ws_need, None) == -1
+    assert L.coli_moe_layer(None, C.byref(w), p, 8, p, None, None, p, ws_need, None) == -1
+    # misaligned pointers
+    assert L.coli_moe_layer(C.byref(c), C.byref(_w(q, experts=FAKE + 8)), p, 8, p, None, None, p, ws_need,
+                            None) == -4
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), C.c_void_p(FAKE + 4), 8, p, None, None, p, ws_need,
+                            None) == -4
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 8, p, None, None, C.c_void_p(FAKE + 64), ws_need,
+                            None) == -4
+    # workspace too small or missing
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 8, p, None, None, p, ws_need - 1, None) == -3
+    assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 8, p, None, None, None, ws_need, None) == -3
+    assert L.coli_moe_ffn(C.byref(c), C.byref(w), p, 8, p, p, p, p, p, p, p, p, 16, None) == -3
+    assert L.coli_moe_route(C.byref(c), C.byref(w), p, 8, p, p, p, 16, None) == -3
+    # quantize
+    assert L.coli_moe_quantize_q8_0(p, 4, 48, p, p, None) == -2
+    assert L.coli_moe_quantize_q8_0(p, -1, 64, p, p, None) == -1
+    assert L.coli_moe_quantize_q8_0(p, 0, 64, None, None, None) == 0
+    assert L.coli_moe_quantize_q8_0(C.c_void_p(FAKE + 4), 4, 64, p, p, None) == -4
+    # profiled: wrong event count
+    arr = (C.c_void_p * 3)(p, p, p)
+    assert L.coli_moe_layer_profiled(C.byref(c), C.byref(w), p, 8, p, p, ws_need, None, arr, 3) == -1
