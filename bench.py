@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer on one MI355X.
+
+A step is one whole layer (route, group, quantise, gate/up, down, combine: every
+row of the hot path) over one batch of T synthetic tokens, on the stacked layer
+l = step mod L, so that consecutive steps stream different weights (the stack is
+larger than the 256 MB Infinity Cache). Inputs are resident in HBM before the
+timed region. Default workload: the OLMoE-scale decode layer (hidden 2048, expert
+FFN 1024, 64 experts, top-8 sigmoid router, int4 per-row weights, Q8_0
+activations), T = 16, 8 stacked layers; T = 1 and 4 are reported in "sweep".
+
+Prints ONE JSON line (rank 0). Extra detail goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, AMD public specification
+DOMINANT_STAGE = "ffn_gate_up"
+KERNEL_SOURCES = ["quantized_moe_sigmoid_amd/csrc/ffn_gemv.hip", "quantized_moe_sigmoid_amd/csrc/coli_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, T: int):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC
+    summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_T{T}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Stack:
+    """L stacked layers of one workload, resident on the device."""
+
+    def __init__(self, wl_index: int, layers: int, wbits: int | None = None):
+        import numpy as np
+        import torch
+        import quantized_moe_sigmoid_amd as q
+        import synth
+        import synth.device
+
+        self.wl = dict(synth.WORKLOADS[wl_index])
+        if wbits is not None:
+            self.wl["wbits"] = wbits
+        wl = self.wl
+        self.cfg = q.make_cfg(**wl)
+        self.blob = q.blob_bytes(self.cfg)
+        self.L = layers
+        self.dev = torch.device("cuda:0")
+        ne = wl["n_experts"] + (1 if wl["has_shared"] else 0)
+        self.ne = ne
+        self.layers = []
+        for l in range(layers):
+            seed = synth.workload_seed(wl_index, l)
+            blobs = torch.empty(ne * self.blob, dtype=torch.uint8, device=self.dev)
+            synth.device.fill_blobs(blobs, seed, l, 0, ne, self.blob, wl["wbits"])
+            inp = synth.layer_inputs(seed, l, tokens=1, hidden=wl["hidden"], ffn=wl["ffn"],
+                                     n_experts=wl["n_experts"], has_shared=wl["has_shared"], wbits=wl["wbits"],
+                                     zipf=wl.get("zipf", False), with_blobs=False)
+            up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+            w = q.Weights(blobs, up(inp["scales"]), up(inp["router_w"]), up(inp["router_bias"]))
+            self.layers.append((seed, w))
+        torch.cuda.synchronize()
+
+    def inputs(self, T: int):
+        import torch
+        import synth
+        xs = []
+        for l, (seed, _) in enumerate(self.layers):
+            xs.append(torch.from_numpy(synth.activations(seed, l, T, self.wl["hidden"])).to(self.dev))
+        return xs
+
+    def union_sizes(self, xs):
+        """Distinct routed experts U of each layer for these inputs (from the library's own grouping)."""
+        import torch
+        import quantized_moe_sigmoid_amd as q
+        T = xs[0].shape[0]
+        E, k = self.wl["n_experts"], self.wl["top_k"]
+        ws = q.alloc_workspace(self.cfg, T, self.dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=self.dev)
+        tw = torch.empty((T, k), dtype=torch.float32, device=self.dev)
+        cnt = torch.empty(E, dtype=torch.int32, device=self.dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=self.dev)
+        perm = torch.empty(T * k, dtype=torch.int32, device=self.dev)
+        act = torch.empty(E, dtype=torch.int32, device=self.dev)
+        na = torch.empty(1, dtype=torch.int32, device=self.dev)
+        us = []
+        for (seed, w), x in zip(self.layers, xs):
+            q.route(self.cfg, w, x, idx, tw, ws)
+            q.group(self.cfg, idx, T, cnt, off, perm, act, na)
+            us.append(int(na.item()))
+        return us
+
+
+def gateup_bytes(wl, U: int, T: int) -> int:
+    """Algorithmic HBM bytes of one gate/up launch: the packed gate and up rows plus their
+    fp32 scales of the U routed (+ shared) experts, the Q8_0 activations read once, and
+    the requantised h written once."""
+    H, F, k, wb = wl["hidden"], wl["ffn"], wl["top_k"], wl["wbits"]
+    S = 1 if wl["has_shared"] else 0
+    nexp = U + S
+    weights = nexp * 2 * F * (H * wb // 8 + 4)
+    acts = T * (H + 8 * (H // 32))
+    rows_out = T * k + S * T
+    hout = rows_out * (F + 8 * (F // 32))
+    return weights + acts + hout
+
+
+def layer_weight_bytes(wl, U: int) -> int:
+    """Packed weights + per-row scales of the experts one layer call streams."""
+    H, F, wb = wl["hidden"], wl["ffn"], wl["wbits"]
+    nexp = U + (1 if wl["has_shared"] else 0)
+    return nexp * (2 * F * (H * wb // 8) + H * (F * wb // 8) + 4 * (2 * F + H))
+
+
+def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
+    import torch
+    import quantized_moe_sigmoid_amd as q
+    xs = stack.inputs(T)
+    L = stack.L
+    ws = q.alloc_workspace(stack.cfg, T, stack.dev)
+    outs = [torch.empty((T, stack.wl["hidden"]), dtype=torch.float32, device=stack.dev) for _ in range(L)]
+    stream = torch.cuda.Stream(stack.dev)
+
+    def step(i):
+        l = i % L
+        q.layer(stack.cfg, stack.layers[l][1], xs[l], outs[l], ws, stream=stream)
+
+    graph = None
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 1)):
+            step(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(L):
+                step(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    reps = max(1, steps // L) if use_graph else steps
+    nsteps = reps * L if use_graph else steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        if use_graph:
+            for _ in range(reps):
+                graph.replay()
+        else:
+            for i in range(steps):
+                step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / nsteps
+
+    # per-stage durations with HIP events on the launch stream
+    ns = q.num_stages()
+    names = [q.stage_name(i) for i in range(ns)]
+    acc = [0.0] * ns
+    nprof = min(steps, 8 * L)
+    with torch.cuda.stream(stream):
+        for i in range(nprof):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
+            l = i % L
+            q.layer_profiled(stack.cfg, stack.layers[l][1], xs[l], outs[l], ws, ev, stream=stream)
+            stream.synchronize()
+            for s in range(ns):
+                acc[s] += ev[s].elapsed_time(ev[s + 1])
+    stage_ms = {names[s]: acc[s] / nprof for s in range(ns)}
+    us = stack.union_sizes(xs)
+    return dict(T=T, ms=ms, steps=nsteps, stage_ms=stage_ms, U=us)
+
+
+def cpu_baseline(stack, T: int, budget_s: float):
+    """The oracle (plain C, OpenMP) timed on host cores on layer 0 of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    wl = stack.wl
+    seed, _ = stack.layers[0]
+    inp = synth.layer_inputs(seed, 0, tokens=T, hidden=wl["hidden"], ffn=wl["ffn"], n_experts=wl["n_experts"],
+                             has_shared=wl["has_shared"], wbits=wl["wbits"], zipf=wl.get("zipf", False))
+    cfg = oracle.make_cfg(**wl)
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer(cfg, inp["blobs"], inp["scales"], inp["router_w"], inp["router_bias"], inp["x"])
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=T * calls / el, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"{calls} oracle calls of layer 0 at T={T} ({el:.1f} s wall)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--wbits", type=int, default=None)
+    ap.add_argument("--tokens", type=str, default=None, help="comma list of T; the last is the headline")
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's sharding across GPUs "
+              "is a design note, not built", file=sys.stderr)
+        sys.exit(2)
+
+    import synth
+    wl0 = synth.WORKLOADS[args.config]
+    Ts = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl0["tokens"])
+    stack = Stack(args.config, args.layers, args.wbits)
+    wl = stack.wl
+    results = []
+    for T in Ts:
+        r = run_T(stack, T, args.steps, args.warmup, not args.no_graph)
+        U = sum(r["U"]) / len(r["U"])
+        r["U_mean"] = U
+        r["tok_s"] = T / (r["ms"] * 1e-3)
+        gu_ms = r["stage_ms"][DOMINANT_STAGE]
+        # algorithmic bytes of the dominant kernel per launch, averaged over the stacked layers
+        gb = sum(gateup_bytes(wl, u, T) for u in r["U"]) / len(r["U"])
+        r["gateup_bytes"] = gb
+        r["gateup_gbs"] = gb / (gu_ms * 1e-3) / 1e9
+        r["layer_weight_gbs"] = (sum(layer_weight_bytes(wl, u) for u in r["U"]) / len(r["U"])) / (r["ms"] * 1e-3) / 1e9
+        results.append(r)
+        log(f"T={T}: {r['ms']*1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, U={U:.1f}, gate/up {gu_ms*1e3:.1f} us "
+            f"= {r['gateup_gbs']:.0f} GB/s, layer weights {r['layer_weight_gbs']:.0f} GB/s; stages(us) " +
+            ", ".join(f"{k}={v*1e3:.1f}" for k, v in r["stage_ms"].items()))
+    head = results[-1]
+    T = head["T"]
+    ach = head["gateup_gbs"]
+    traffic = read_traffic(wl["name"], T)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(stack, T, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+    line = {
+        "metric": "MoE-layer tokens/s (decode)",
+        "value": round(head["tok_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xint4",
+        "data": "synthetic (seeded SplitMix64; random int weights, N(0,1) activations)",
+        "config": {"workload": wl["name"], "hidden": wl["hidden"], "ffn": wl["ffn"], "n_experts": wl["n_experts"],
+                   "top_k": wl["top_k"], "n_group": wl["n_group"], "topk_group": wl["topk_group"],
+                   "has_shared": wl["has_shared"], "wbits": wl["wbits"], "tokens": T,
+                   "stacked_layers": stack.L, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "gemv_kernel<gate/up>", "bytes_per_launch": int(head["gateup_bytes"]),
+                     "avg_launch_us": round(head["stage_ms"][DOMINANT_STAGE] * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "sweep": [{"T": r["T"], "tokens_per_s": round(r["tok_s"], 1), "us_per_step": round(r["ms"] * 1e3, 2),
+                   "U_mean": r["U_mean"], "gate_up_GBps": round(r["gateup_gbs"], 1),
+                   "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
+                   "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}} for r in results],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

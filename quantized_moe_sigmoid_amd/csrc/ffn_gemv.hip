@@ -119,6 +119,77 @@ __device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<
   }
 }
 
+// Split form of chunk_dot for the batched kernel: the unpacked weight bytes of a
+// chunk (offset-binary, 0..15 / 0..3, or raw int8) and the activation registers of
+// one token are kept separately so that one unpack serves every token.
+template <int WB>
+struct Unp {
+  static constexpr int N = (WB == 2) ? 16 : 8;  // dwords of unpacked weights per chunk
+};
+
+template <int WB>
+__device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK / 4], int (&u)[Unp<WB>::N]) {
+  if constexpr (WB == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint32_t t = wq[i] ^ 0x88888888u;
+      u[i] = (int)(t & 0x0F0F0F0Fu);
+      u[4 + i] = (int)((t >> 4) & 0x0F0F0F0Fu);
+    }
+  } else if constexpr (WB == 8) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) u[i] = (int)wq[i];
+  } else {
+    // block blk, element dword d (elements 4d..4d+3) = field m of source dword h, d = 2m + h
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const uint32_t t = wq[2 * blk + h] ^ 0xAAAAAAAAu;
+#pragma unroll
+        for (int m = 0; m < 4; m++) u[8 * blk + 2 * m + h] = (int)((t >> (2 * m)) & 0x03030303u);
+      }
+  }
+}
+
+// activation registers of one chunk for one token: Q8_0 bytes and {d, sum} per block
+template <int WB>
+struct Act {
+  int x[Unp<WB>::N];
+  int2 ds[Fmt<WB>::BPC];
+};
+
+template <int WB>
+__device__ __forceinline__ void load_act(const int8_t *xa, const int2 *xd, Act<WB> &a) {
+#pragma unroll
+  for (int i = 0; i < Unp<WB>::N / 4; i++) {
+    const int4 v = *reinterpret_cast<const int4 *>(xa + 16 * i);
+    a.x[4 * i] = v.x;
+    a.x[4 * i + 1] = v.y;
+    a.x[4 * i + 2] = v.z;
+    a.x[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int b = 0; b < Fmt<WB>::BPC; b++) a.ds[b] = xd[b];
+}
+
+template <int WB>
+__device__ __forceinline__ float dot_unpacked(const int (&u)[Unp<WB>::N], const Act<WB> &a) {
+  constexpr int OFF = (WB == 4) ? 8 : (WB == 2) ? 2 : 0;  // offset-binary bias of the weights
+  float r = 0.0f;
+#pragma unroll
+  for (int b = 0; b < Fmt<WB>::BPC; b++) {
+    int acc = -OFF * a.ds[b].y;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc = dot4(u[8 * b + i], a.x[8 * b + i], acc);
+    if (b == 0)
+      r = __int_as_float(a.ds[b].x) * (float)acc;
+    else
+      r += __int_as_float(a.ds[b].x) * (float)acc;
+  }
+  return r;
+}
+
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
 // Resolve a grid slot to (expert, number of tokens, segment start). Returns false
@@ -295,11 +366,244 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batched GEMV (the hot path for the common shapes). Same arithmetic and the same
+// per-(row, token) summation tree as gemv_kernel; what changes is the schedule:
+// each lane issues all weight loads of a batch of rows at once (up to 16 chunk
+// loads, i.e. 16 KB in flight per wavefront), then computes every (row, token)
+// partial sum of the batch, then reduces them across the LPR lanes of a row with
+// a reduce-scatter (each shuffle step halves the values a lane carries), so the
+// cross-lane cost is about one shuffle per value instead of log2(LPR).
+template <int A, int B>
+struct cmin {
+  static constexpr int v = A < B ? A : B;
+};
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Sum a[0..V) over the lanes of an aligned group of 2*O lanes. Scatter steps keep
+// half of the values per lane; once one value is left the remaining steps are a
+// plain butterfly. On return a[0..kept) hold full sums of original indices
+// base .. base + kept - 1.
+template <int V, int O>
+__device__ __forceinline__ void reduce_scatter(float *a, int lane, int &base) {
+  if constexpr (O >= 1) {
+    if constexpr (V > 1) {
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < V / 2; i++) {
+        const float send = up ? a[i] : a[i + V / 2];
+        const float keep = up ? a[i + V / 2] : a[i];
+        a[i] = keep + __shfl_xor(send, O);
+      }
+      if (up) base += V / 2;
+      reduce_scatter<V / 2, O / 2>(a, lane, base);
+    } else {
+      a[0] += __shfl_xor(a[0], O);
+      reduce_scatter<1, O / 2>(a, lane, base);
+    }
+  }
+}
+
+struct FastCtx {
+  const uint8_t *mat0, *mat1;
+  int64_t rb;        // packed bytes per row
+  int K, nkb;
+  const int8_t *xs;  // LDS activations [ntmax][K]
+  const int2 *xds;   // LDS block scales [ntmax][nkb]
+  float *obuf;       // LDS results [NMAT][8][TILE]
+  int r0;            // first row of the tile
+};
+
+template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC>
+__device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, int wv) {
+  constexpr int RPI = WAVE / LPR;
+  constexpr int CW = Fmt<WB>::CHUNK / 4;
+  constexpr int BPC = Fmt<WB>::BPC;
+  constexpr int LPC = Fmt<WB>::CHUNK / 16;
+  constexpr int TILE = 4 * WR;
+  // rows per lane and step: up to 16 chunk loads in flight, at most 32 accumulators
+  constexpr int BR_LOAD = cmin<8, (16 / (NMAT * LPC) > 0 ? 16 / (NMAT * LPC) : 1)>::v;
+  constexpr int BR_ACC = (32 / (NMAT * NTC) > 0) ? 32 / (NMAT * NTC) : 1;
+  constexpr int BR_ROWS = (WR / RPI > 0) ? WR / RPI : 1;
+  constexpr int BR = cmin<cmin<BR_LOAD, BR_ACC>::v, BR_ROWS>::v;
+  constexpr int RPB = BR * RPI;  // rows of the wave per batch
+  constexpr int V = BR * NMAT * NTC;
+  constexpr int SCAT = cmin<ilog2(V), ilog2(LPR)>::v;
+  constexpr int KEPT = V >> SCAT;
+  constexpr int WMASK = (LPR >> SCAT) - 1;
+  const int rs = lane / LPR, sub = lane % LPR;
+
+  for (int b0 = 0; b0 < WR; b0 += RPB) {
+    int64_t roff[BR];
+#pragma unroll
+    for (int j = 0; j < BR; j++) {
+      int rw = b0 + j * RPI + rs;
+      rw = rw < WR ? rw : WR - 1;
+      roff[j] = (int64_t)(c.r0 + wv * WR + rw) * c.rb;
+    }
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) acc[i] = 0.0f;
+#pragma unroll 1
+    for (int ci = 0; ci < CPL; ci++) {
+      const int ch = sub + ci * LPR;
+      uint32_t w[BR][NMAT][CW];
+#pragma unroll
+      for (int j = 0; j < BR; j++)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+          load_chunk<WB>((m == 0 ? c.mat0 : c.mat1) + roff[j] + (int64_t)ch * Fmt<WB>::CHUNK, w[j][m]);
+      Act<WB> act[NTC];
+#pragma unroll
+      for (int t = 0; t < NTC; t++)
+        if (t < nt) load_act<WB>(c.xs + t * c.K + ch * BPC * QK, c.xds + t * c.nkb + ch * BPC, act[t]);
+#pragma unroll
+      for (int j = 0; j < BR; j++)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) {
+          int u[Unp<WB>::N];
+          unpack_chunk<WB>(w[j][m], u);
+#pragma unroll
+          for (int t = 0; t < NTC; t++)
+            if (t < nt) acc[(j * NMAT + m) * NTC + t] += dot_unpacked<WB>(u, act[t]);
+        }
+    }
+    int base = 0;
+    reduce_scatter<V, LPR / 2>(acc, lane, base);
+    if ((lane & WMASK) == 0) {
+#pragma unroll
+      for (int i = 0; i < KEPT; i++) {
+        const int o = base + i;
+        const int t = o % NTC, m = (o / NTC) % NMAT, j = o / (NTC * NMAT);
+        const int rw = b0 + j * RPI + rs;
+        if (t < nt && rw < WR) c.obuf[(m * 8 + t) * TILE + wv * WR + rw] = acc[i];
+      }
+    }
+  }
+}
+
+template <int WB, int LPR, int CPL, int MODE, int WR>
+__global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
+  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int TILE = 4 * WR;
+  static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
+
+  int e, n, beg;
+  bool shared;
+  if (!resolve_slot(a, blockIdx.y, e, n, beg, shared)) return;
+
+  const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
+  const int nkb = K / QK;
+  const int P = a.T * a.k;
+  const uint8_t *blob = a.experts + (int64_t)e * a.blob_bytes;
+  const int64_t rbh = row_bytes(WB, a.H);
+  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+
+  extern __shared__ __align__(16) char smem[];
+  FastCtx c;
+  c.mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+  c.mat1 = blob + (int64_t)a.F * rbh;
+  c.rb = row_bytes(WB, K);
+  c.K = K;
+  c.nkb = nkb;
+  int8_t *xs = reinterpret_cast<int8_t *>(smem);
+  int2 *xds = reinterpret_cast<int2 *>(smem + (size_t)ntmax * K);
+  float *obuf = reinterpret_cast<float *>(xds + (size_t)ntmax * nkb);
+  int *orow = reinterpret_cast<int *>(obuf + NMAT * 8 * TILE);
+  c.xs = xs;
+  c.xds = xds;
+  c.obuf = obuf;
+  c.r0 = blockIdx.x * TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
+  const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+
+  for (int tc = 0; tc < n; tc += ntmax) {
+    const int nt = min(ntmax, n - tc);
+    if (tid < 8) {
+      int out = -1, act = 0;
+      if (tid < nt) {
+        const int i = tc + tid;
+        out = shared ? P + i : a.perm[beg + i];
+        act = (MODE == MODE_GATEUP) ? (shared ? i : out / a.k) : out;
+      }
+      orow[tid] = out;
+      orow[8 + tid] = act;
+    }
+    __syncthreads();
+    const int v16 = K / 16;
+    for (int i = tid; i < nt * v16; i += 256) {
+      const int t = i / v16, ch = i % v16;
+      *reinterpret_cast<int4 *>(xs + t * K + ch * 16) =
+          *reinterpret_cast<const int4 *>(asrc + (int64_t)orow[8 + t] * K + ch * 16);
+    }
+    for (int i = tid; i < nt * nkb; i += 256) {
+      const int t = i / nkb, b = i % nkb;
+      xds[t * nkb + b] = dsrc[(int64_t)orow[8 + t] * nkb + b];
+    }
+    __syncthreads();
+    if (nt <= 1)
+      fast_pass<WB, NMAT, LPR, CPL, WR, 1>(c, nt, lane, wv);
+    else if (nt <= 2)
+      fast_pass<WB, NMAT, LPR, CPL, WR, 2>(c, nt, lane, wv);
+    else if (nt <= 4)
+      fast_pass<WB, NMAT, LPR, CPL, WR, 4>(c, nt, lane, wv);
+    else if constexpr (WB != 2)
+      fast_pass<WB, NMAT, LPR, CPL, WR, 8>(c, nt, lane, wv);
+    __syncthreads();
+    // epilogue over the tile's rows x nt tokens
+    if constexpr (MODE == MODE_GATEUP) {
+      const float *sg = sc, *su = sc + a.F;
+      for (int p = tid; p < nt * TILE; p += 256) {  // one Q8_0 block of h per 32 consecutive lanes
+        const int t = p / TILE, i = p % TILE, r = c.r0 + i;
+        const float g = sg[r] * obuf[(0 * 8 + t) * TILE + i];
+        const float u = su[r] * obuf[(1 * 8 + t) * TILE + i];
+        const float v = (g / (1.0f + expf(-g))) * u;
+        float am = fabsf(v);
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        const float d = am / 127.0f;
+        int q = 0;
+        if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
+        int sum = q;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+        const int out = orow[t];
+        a.hq[(int64_t)out * a.F + r] = (int8_t)q;
+        if ((i & 31) == 0) a.hds[(int64_t)out * (a.F / QK) + r / QK] = make_int2(__float_as_int(d), sum);
+      }
+    } else {
+      const float *sd = sc + 2 * a.F;
+      for (int p = tid; p < nt * TILE; p += 256) {
+        const int t = p / TILE, i = p % TILE, r = c.r0 + i;
+        a.ypair[(int64_t)orow[t] * a.H + r] = sd[r] * obuf[t * TILE + i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // lanes per row: largest power of two <= 64 dividing the chunks per row
 static int pick_lpr(int nchunk) {
   int l = 64;
   while (l > 1 && nchunk % l) l >>= 1;
   return l;
+}
+
+template <int WB, int LPR, int CPL, int MODE>
+static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int K, hipStream_t s) {
+  constexpr int WR = (MODE == MODE_DOWN && LPR < 64) ? 16 : 8;
+  constexpr int TILE = 4 * WR;
+  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+  if (nrows % TILE) return hipErrorNotSupported;
+  const int ntmax = min(WB == 2 ? 4 : 8, a.T);
+  const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(int2) + (size_t)NMAT * 8 * TILE * sizeof(float) +
+                     16 * sizeof(int);
+  dim3 grid(nrows / TILE, slots_grid.y);
+  hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR>), grid, dim3(256), lds, s, a, ntmax);
+  return hipGetLastError();
 }
 
 template <int WB, int MODE>
@@ -309,7 +613,19 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   const int nkb = K / QK;
   const int nchunk = nkb / Fmt<WB>::BPC;
   const int lpr = pick_lpr(nchunk);
+  const int cpl = nchunk / lpr;
   const int slots = a.has_shared + min(a.E, a.T * a.k);
+  // the batched kernel for the shapes it is instantiated for
+  if (lpr == 64 || lpr == 32) {
+    hipError_t r = hipErrorNotSupported;
+    const dim3 sg(1, slots);
+    if (lpr == 64 && cpl == 1) r = launch_fast<WB, 64, 1, MODE>(a, sg, NROWS, K, s);
+    else if (lpr == 64 && cpl == 2) r = launch_fast<WB, 64, 2, MODE>(a, sg, NROWS, K, s);
+    else if (lpr == 64 && cpl == 3) r = launch_fast<WB, 64, 3, MODE>(a, sg, NROWS, K, s);
+    else if (lpr == 32 && cpl == 1) r = launch_fast<WB, 32, 1, MODE>(a, sg, NROWS, K, s);
+    else if (lpr == 32 && cpl == 3) r = launch_fast<WB, 32, 3, MODE>(a, sg, NROWS, K, s);
+    if (r != hipErrorNotSupported) return r;
+  }
   dim3 grid(NROWS / GEMV_ROWS, slots);
   const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(int2) +
                      (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);

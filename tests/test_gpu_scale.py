@@ -1,0 +1,130 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Expert blobs are generated on the device (synth.device, byte-identical to the host
+generator, checked here); the oracle regenerates on the host only the experts the
+sampled tokens route to and evaluates those tokens one by one. Router indices are
+compared for every token, layer outputs for the sampled tokens.
+"""
+import numpy as np
+import pytest
+
+import gpu_util as gu
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import quantized_moe_sigmoid_amd as q
+    import synth.device
+    q.lib()
+    synth.device.lib()
+    return q, oracle
+
+
+def _run(env, wl_index, T, sample, wbits=None, layer=0):
+    import torch
+    import synth.device
+    q, orc = env
+    wl = gu.workload_cfg(wl_index, wbits)
+    seed = synth.workload_seed(wl_index, layer)
+    H, F, E, S = wl["hidden"], wl["ffn"], wl["n_experts"], 1 if wl["has_shared"] else 0
+    cfg = q.make_cfg(**wl)
+    blob = q.blob_bytes(cfg)
+    d = gu.dev()
+    blobs = torch.empty((E + S) * blob, dtype=torch.uint8, device=d)
+    synth.device.fill_blobs(blobs, seed, layer, 0, E + S, blob, wl["wbits"])
+    inp = synth.layer_inputs(seed, layer, tokens=T, hidden=H, ffn=F, n_experts=E, has_shared=wl["has_shared"],
+                             wbits=wl["wbits"], zipf=wl.get("zipf", False), with_blobs=False)
+    w = q.Weights(blobs, gu.to_dev(inp["scales"]), gu.to_dev(inp["router_w"]), gu.to_dev(inp["router_bias"]))
+    out, idx, tw = gu.run_layer(wl, w, inp["x"])
+    ocfg = orc.make_cfg(**wl)
+    ridx, rw = orc.route(ocfg, inp["router_w"], inp["router_bias"], inp["x"])
+    assert np.array_equal(idx, ridx)
+    assert gu.ulp_diff_f32(tw, rw).max() <= 1
+    # the oracle on the sampled tokens, with only their experts regenerated on the host
+    toks = sorted(set(int(t) for t in sample))
+    need = sorted(set(int(e) for t in toks for e in ridx[t]))
+    remap = {e: i for i, e in enumerate(need)}
+    hb = [synth.expert_blob(seed, layer, e, H, F, wl["wbits"]) for e in need]
+    hs = [inp["scales"][e] for e in need]
+    if S:
+        hb.append(synth.expert_blob(seed, layer, E, H, F, wl["wbits"]))
+        hs.append(inp["scales"][E])
+    # the device blobs equal the host generator's bytes
+    for e in need[:2] + ([E] if S else []):
+        got = blobs[e * blob:(e + 1) * blob].cpu().numpy()
+        assert np.array_equal(got, synth.expert_blob(seed, layer, e, H, F, wl["wbits"]))
+    sub = orc.make_cfg(hidden=H, ffn=F, n_experts=len(need), top_k=wl["top_k"], rsf=wl["rsf"],
+                       has_shared=wl["has_shared"], wbits=wl["wbits"])
+    sidx = np.vectorize(remap.get)(ridx[toks]).astype(np.int32)
+    ref = orc.ffn(sub, np.stack(hb), np.stack(hs), inp["x"][toks], sidx, rw[toks])
+    err = gu.rel_err_per_token(out[toks], ref)
+    assert err.max() <= TOL, err
+    assert np.all(np.isfinite(out))
+    return out, idx
+
+
+def test_olmoe_decode_full(env):
+    for T in (1, 4, 16):
+        _run(env, 1, T, range(T))
+
+
+def test_glm_decode_full(env):
+    for T in (1, 16):
+        _run(env, 2, T, [0, T // 2, T - 1])
+
+
+def test_glm_prefill_full_sampled(env):
+    _, idx = _run(env, 3, 2048, [0, 1, 777, 2047])
+    cnt = np.bincount(idx.ravel(), minlength=256)
+    assert cnt.max() > 100 and (cnt == 0).sum() >= 1, (cnt.max(), (cnt == 0).sum())
+
+
+@pytest.mark.parametrize("wbits", [8, 2])
+def test_glm_verify_lowbit_full(env, wbits):
+    _run(env, 4, 3, [0, 1, 2], wbits=wbits)
+
+
+def test_graph_replay_matches_eager(env):
+    """A captured graph of several layer calls, replayed several times with eager work
+    and synchronisations in between, reproduces the eager results bit for bit."""
+    import torch
+    q, _ = env
+    wl = gu.workload_cfg(1)
+    cfg = q.make_cfg(**wl)
+    d = gu.dev()
+    T, L = 4, 3
+    layers, xs, outs = [], [], []
+    for l in range(L):
+        seed = synth.workload_seed(1, l)
+        inp = synth.layer_inputs(seed, l, tokens=T, hidden=2048, ffn=1024, n_experts=64, has_shared=False, wbits=4)
+        layers.append(gu.upload_layer(inp))
+        xs.append(gu.to_dev(inp["x"]))
+        outs.append(torch.empty((T, 2048), dtype=torch.float32, device=d))
+    ws = q.alloc_workspace(cfg, T, d)
+    eager = []
+    for l in range(L):
+        q.layer(cfg, layers[l], xs[l], outs[l], ws)
+        eager.append(outs[l].clone())
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(d)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for l in range(L):
+            q.layer(cfg, layers[l], xs[l], outs[l], ws, stream=s)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(outs[l].view(torch.int32), eager[l].view(torch.int32)), (rep, l)
+        _ = torch.randn(1000, device=d).sum().item()  # eager work between replays
