@@ -29,20 +29,39 @@ WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit);
 // number of K splits of the router logits for T tokens
 int32_t route_ksplit(const coli_moe_cfg &c, int32_t T);
 
+struct GroupOut {
+  int32_t *cnt, *off, *perm, *active, *nact;
+};
+
+constexpr int LOCAL_GROUP_MAX_P = 512;  // pairs a GEMV workgroup groups by itself (decode-sized batches)
+
 // ---- launchers (host side, one per kernel family); return hipError_t
-hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, int2 *ds,
-                       hipStream_t s);
-hipError_t launch_route(const coli_moe_cfg &c, const float *x, int32_t T, const float *W, const float *bias,
-                        double *logits, int32_t ksplit, int32_t *idx, float *w, hipStream_t s, hipEvent_t mid);
+hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, int2 *ds, hipStream_t s);
+
+struct RouteLaunch {
+  const coli_moe_cfg *cfg;
+  const float *x;
+  int32_t T;
+  const float *W, *bias;
+  double *logits;
+  int32_t ksplit;
+  int32_t *idx;
+  float *w;
+  int8_t *xq;        // quantise x into xq/xds in the selection kernel when non-null
+  int2 *xds;
+};
+hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid);
 hipError_t launch_group(const coli_moe_cfg &c, const int32_t *idx, int32_t T, int32_t *cnt, int32_t *off,
                         int32_t *perm, int32_t *active, int32_t *nact, hipStream_t s);
+bool group_supported(int P, int E);
 
 struct FfnArgs {
   const uint8_t *experts;
   const float *scales;
   int64_t blob_bytes;
   int32_t H, F, E, k, T, has_shared;
-  const int32_t *off, *perm, *active, *nact;
+  const int32_t *off, *perm, *active, *nact;  // grouping arrays (read when idx == nullptr)
+  const int32_t *idx;  // route [T][k]: each workgroup groups locally when set (T*k <= LOCAL_GROUP_MAX_P)
   const int8_t *xq;   // [T][H]
   const int2 *xds;    // [T][H/32] {d bits, block sum}
   int8_t *hq;         // [P+T][F]

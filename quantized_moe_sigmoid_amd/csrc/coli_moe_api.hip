@@ -6,7 +6,6 @@
 #include "coli_internal.h"
 
 namespace coli {
-bool group_supported(int P, int E);
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -85,13 +84,16 @@ static Tp *at(void *ws, size_t off) {
   return reinterpret_cast<Tp *>(static_cast<char *>(ws) + off);
 }
 
+// Expert FFNs and combine. With quantize_x the standalone Q8_0 kernel runs first;
+// otherwise x was quantised by the routing kernel.
 static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const float *x, int32_t T,
                        const float *topk_w, const int32_t *off, const int32_t *perm, const int32_t *active,
-                       const int32_t *nact, float *out, void *ws, const WsLayout &L, hipStream_t s,
-                       hipEvent_t *ev) {
+                       const int32_t *nact, const int32_t *local_idx, float *out, void *ws, const WsLayout &L,
+                       hipStream_t s, hipEvent_t *ev, bool quantize_x) {
   int st;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
-  if ((st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), nullptr, at<int2>(ws, L.xds), s)))) return st;
+  if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), nullptr, at<int2>(ws, L.xds), s))))
+    return st;
   FfnArgs a{};
   a.experts = static_cast<const uint8_t *>(w.experts);
   a.scales = w.scales;
@@ -106,6 +108,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.perm = perm;
   a.active = active;
   a.nact = nact;
+  a.idx = local_idx;
   a.xq = at<int8_t>(ws, L.xq);
   a.xds = at<int2>(ws, L.xds);
   a.hq = at<int8_t>(ws, L.hq);
@@ -121,8 +124,8 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   return COLI_OK;
 }
 
-// stage order of coli_moe_layer_profiled
-static const char *const kStages[] = {"route_logits", "route_topk", "group", "quantize_x",
+// stage order of coli_moe_layer_profiled; a stage fused into the previous kernel is empty
+static const char *const kStages[] = {"route_logits", "route_select", "group", "quantize_x",
                                       "ffn_gate_up", "ffn_down", "combine"};
 static constexpr int kNumStages = 7;
 
@@ -143,15 +146,28 @@ static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t *idx = idx_opt ? idx_opt : at<int32_t>(ws, L.idx);
   float *tw = w_opt ? w_opt : at<float>(ws, L.w);
-  if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
-  if ((st = dev(launch_route(*cfg, x, T, w->router_w, w->router_bias, at<double>(ws, L.logits), ks, idx, tw, s,
-                             ev ? ev[1] : nullptr))))
-    return st;
-  if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
   int32_t *off = at<int32_t>(ws, L.off), *perm = at<int32_t>(ws, L.perm), *act = at<int32_t>(ws, L.active),
-          *nact = at<int32_t>(ws, L.nact);
-  if ((st = dev(launch_group(*cfg, idx, T, at<int32_t>(ws, L.cnt), off, perm, act, nact, s)))) return st;
-  return ffn_enqueue(*cfg, *w, x, T, tw, off, perm, act, nact, out, ws, L, s, ev ? ev + 3 : nullptr);
+          *nact = at<int32_t>(ws, L.nact), *cnt = at<int32_t>(ws, L.cnt);
+  RouteLaunch r{};
+  r.cfg = cfg;
+  r.x = x;
+  r.T = T;
+  r.W = w->router_w;
+  r.bias = w->router_bias;
+  r.logits = at<double>(ws, L.logits);
+  r.ksplit = ks;
+  r.idx = idx;
+  r.w = tw;
+  r.xq = at<int8_t>(ws, L.xq);
+  r.xds = at<int2>(ws, L.xds);
+  // decode-sized batches: every GEMV workgroup groups the route itself
+  const bool local = (int64_t)T * cfg->top_k <= LOCAL_GROUP_MAX_P;
+  if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
+  if ((st = dev(launch_route(r, s, ev ? ev[1] : nullptr)))) return st;
+  if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
+  if (!local && (st = dev(launch_group(*cfg, idx, T, cnt, off, perm, act, nact, s)))) return st;
+  return ffn_enqueue(*cfg, *w, x, T, tw, off, perm, act, nact, local ? idx : nullptr, out, ws, L, s,
+                     ev ? ev + 3 : nullptr, false);
 }
 
 }  // namespace coli
@@ -200,8 +216,17 @@ int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const flo
   const WsLayout L = ws_layout(*cfg, T, ks);
   if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
   if (!aligned(workspace, 256)) return COLI_E_ALIGN;
-  return dev(launch_route(*cfg, x, T, w->router_w, w->router_bias, at<double>(workspace, L.logits), ks, topk_idx,
-                          topk_w, static_cast<hipStream_t>(stream), nullptr));
+  RouteLaunch r{};
+  r.cfg = cfg;
+  r.x = x;
+  r.T = T;
+  r.W = w->router_w;
+  r.bias = w->router_bias;
+  r.logits = at<double>(workspace, L.logits);
+  r.ksplit = ks;
+  r.idx = topk_idx;
+  r.w = topk_w;
+  return dev(launch_route(r, static_cast<hipStream_t>(stream), nullptr));
 }
 
 int coli_moe_group(const coli_moe_cfg *cfg, const int32_t *topk_idx, int32_t T, int32_t *expert_cnt,
@@ -235,8 +260,8 @@ int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float
   const WsLayout L = ws_layout(*cfg, T, route_ksplit(*cfg, T));
   if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
   if (!aligned(workspace, 256)) return COLI_E_ALIGN;
-  return ffn_enqueue(*cfg, *w, x, T, topk_w, expert_off, pair_perm, active, n_active, out, workspace, L,
-                     static_cast<hipStream_t>(stream), nullptr);
+  return ffn_enqueue(*cfg, *w, x, T, topk_w, expert_off, pair_perm, active, n_active, nullptr, out, workspace, L,
+                     static_cast<hipStream_t>(stream), nullptr, true);
 }
 
 int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,

@@ -192,9 +192,22 @@ __device__ __forceinline__ float dot_unpacked(const int (&u)[Unp<WB>::N], const 
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
-// Resolve a grid slot to (expert, number of tokens, segment start). Returns false
-// if the slot has no work. Slot 0 is the shared expert when there is one.
-__device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, int &e, int &n, int &beg, bool &shared) {
+// Resolve a grid slot to its expert and its pairs. Slot 0 is the shared expert
+// when there is one (every token, output rows P + t); routed slot u is the u-th
+// expert, ascending, with at least one pair. With a.idx set (decode-sized batches,
+// P <= LOCAL_GROUP_MAX_P) the workgroup derives this from the route itself: one
+// wavefront loads the P expert ids, marks them in an LDS bitmap, picks the u-th
+// set bit and lists the expert's pair ids in ascending order with ballots. This
+// replaces the grouping kernel and the chain of dependent loads (active -> offsets
+// -> perm) with one load. Otherwise the grouping arrays are read.
+struct SlotLds {
+  int e, n;
+  uint32_t bits[32];  // E <= 1024
+  int pairs[LOCAL_GROUP_MAX_P];
+};
+
+__device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, SlotLds &L, int &e, int &n, int &beg,
+                                             bool &shared) {
   if (a.has_shared && slot == 0) {
     e = a.E;
     n = a.T;
@@ -202,14 +215,84 @@ __device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, int &e,
     shared = true;
     return n > 0;
   }
-  const int u = slot - a.has_shared;
-  const int na = *a.nact;
-  if (u >= na) return false;
-  e = a.active[u];
-  beg = a.off[e];
-  n = a.off[e + 1] - beg;
   shared = false;
-  return n > 0;
+  const int u = slot - a.has_shared;
+  if (a.idx == nullptr) {
+    const int na = *a.nact;
+    if (u >= na) return false;
+    e = a.active[u];
+    beg = a.off[e];
+    n = a.off[e + 1] - beg;
+    return n > 0;
+  }
+  beg = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = a.T * a.k;
+  if (tid < 64) {
+    constexpr int QD = LOCAL_GROUP_MAX_P / 64;
+    int ev[QD];
+#pragma unroll
+    for (int i = 0; i < QD; i++) {
+      const int p = lane + 64 * i;
+      ev[i] = -1;
+      if (p < P) {
+        const int v = a.idx[p];
+        ev[i] = ((unsigned)v < (unsigned)a.E) ? v : -1;
+      }
+    }
+    if (lane < 32) L.bits[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < QD; i++)
+      if (ev[i] >= 0) atomicOr(&L.bits[ev[i] >> 5], 1u << (ev[i] & 31));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t word = (lane < 32) ? L.bits[lane] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int excl = incl - c;
+    const int total = __shfl(incl, 63);
+    int me = -1;
+    if (excl <= u && u < incl) {
+      uint32_t w = word;
+      for (int i = 0; i < u - excl; i++) w &= w - 1;
+      me = lane * 32 + __ffs((int)w) - 1;
+    }
+    // broadcast the owner's expert (exactly one lane has it when u < total)
+    const uint64_t own = __ballot(me >= 0);
+    const int ex = (u < total && own) ? __shfl(me, __ffsll((long long)own) - 1) : -1;
+    int cnt = 0;
+    if (ex >= 0) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int i = 0; i < QD; i++) {
+        const bool m = ev[i] == ex;
+        const uint64_t b = __ballot(m);
+        if (m) L.pairs[cnt + __popcll(b & below)] = lane + 64 * i;
+        cnt += __popcll(b);
+      }
+    }
+    if (lane == 0) {
+      L.e = ex;
+      L.n = cnt;
+    }
+  }
+  __syncthreads();
+  e = L.e;
+  n = L.n;
+  return e >= 0 && n > 0;
+}
+
+// pair id (row of hq / ypair) of the i-th token of a resolved slot
+__device__ __forceinline__ int slot_pair(const FfnArgs &a, const SlotLds &L, bool shared, int beg, int i) {
+  if (shared) return a.T * a.k + i;
+  return a.idx ? L.pairs[i] : a.perm[beg + i];
 }
 
 template <int WB, int LPR, int MODE>
@@ -221,9 +304,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   constexpr int CW = Fmt<WB>::CHUNK / 4;
   constexpr int BPC = Fmt<WB>::BPC;
 
+  __shared__ SlotLds SL;
   int e, n, beg;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, e, n, beg, shared)) return;
+  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
 
   const int K = (MODE == MODE_GATEUP) ? a.H : a.F;       // inputs per row
   const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;   // output rows per matrix
@@ -258,7 +342,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
       int out = -1, act = 0;
       if (tid < nt) {
         const int i = tc + tid;
-        out = shared ? P + i : a.perm[beg + i];
+        out = slot_pair(a, SL, shared, beg, i);
         act = (MODE == MODE_GATEUP) ? (shared ? i : out / a.k) : out;
       }
       orow[tid] = out;
@@ -489,13 +573,13 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   constexpr int TILE = 4 * WR;
   static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
 
+  __shared__ SlotLds SL;
   int e, n, beg;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, e, n, beg, shared)) return;
+  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
 
   const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
   const int nkb = K / QK;
-  const int P = a.T * a.k;
   const uint8_t *blob = a.experts + (int64_t)e * a.blob_bytes;
   const int64_t rbh = row_bytes(WB, a.H);
   const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
@@ -526,7 +610,7 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
       int out = -1, act = 0;
       if (tid < nt) {
         const int i = tc + tid;
-        out = shared ? P + i : a.perm[beg + i];
+        out = slot_pair(a, SL, shared, beg, i);
         act = (MODE == MODE_GATEUP) ? (shared ? i : out / a.k) : out;
       }
       orow[tid] = out;
