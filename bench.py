@@ -179,22 +179,47 @@ def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / nsteps
 
-    # per-stage durations with HIP events on the launch stream
+    # Per-stage durations: a second timed pass over the same steps, with HIP events
+    # (no system-scope fence, so recording them costs no cache flush) recorded on the
+    # launch stream between the stages of each layer call.
     ns = q.num_stages()
     names = [q.stage_name(i) for i in range(ns)]
     acc = [0.0] * ns
-    nprof = min(steps, 8 * L)
+    nprof = max(L, (min(steps, 8 * L) // L) * L)
+    ev = q.TimingEvents(ns + 1)
     with torch.cuda.stream(stream):
         for i in range(nprof):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
             l = i % L
             q.layer_profiled(stack.cfg, stack.layers[l][1], xs[l], outs[l], ws, ev, stream=stream)
             stream.synchronize()
             for s in range(ns):
-                acc[s] += ev[s].elapsed_time(ev[s + 1])
+                acc[s] += ev.elapsed_ms(s, s + 1)
+    ev.close()
     stage_ms = {names[s]: acc[s] / nprof for s in range(ns)}
     us = stack.union_sizes(xs)
     return dict(T=T, ms=ms, steps=nsteps, stage_ms=stage_ms, U=us)
+
+
+def copy_bandwidth(mbytes: int, reps: int):
+    """Streaming copy of mbytes MiB (synth.device.copy, 16-byte loads and stores):
+    the traffic-calibration kernel of the hardware byte counters and a measured
+    read+write bandwidth beside the HBM peak. Returns GB/s of (read + write)."""
+    import torch
+    import synth.device
+    n = mbytes << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    synth.device.copy(src, dst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        synth.device.copy(src, dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    return 2 * n / dt / 1e9
 
 
 def cpu_baseline(stack, T: int, budget_s: float):
@@ -219,6 +244,75 @@ def cpu_baseline(stack, T: int, budget_s: float):
                 sample=f"{calls} oracle calls of layer 0 at T={T} ({el:.1f} s wall)")
 
 
+def _csv_rows(path_or_dir: str, suffix: str):
+    import csv
+    import glob
+    if os.path.isdir(path_or_dir):
+        files = sorted(glob.glob(os.path.join(path_or_dir, "**", "*" + suffix), recursive=True))
+    else:
+        files = [path_or_dir]
+    if not files:
+        raise SystemExit(f"no *{suffix} under {path_or_dir}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_stats(stats_csv: str, out: str, cmd: str):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel summary."""
+    rows = _csv_rows(stats_csv, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel summary", "", f"Command: `{cmd}`", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str, calib_mb: int, cmd: str):
+    """Per-launch HBM bytes of the dominant kernel from two rocprofv3 --pmc runs.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for the
+    copy kernel of known size (calib_mb MiB read and written per launch)."""
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            a = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+            a[0] += float(r["Counter_Value"])
+            a[1] += 1
+        return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
+
+    fetch = per_kernel(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = per_kernel(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    calib_bytes = calib_mb << 20
+    copy_name = next(k for k in fetch if "copy_kernel" in k)
+    f_fetch = calib_bytes / (fetch[copy_name][0] * 1024.0)
+    f_write = calib_bytes / (write[copy_name][0] * 1024.0)
+    gemv = [k for k in fetch if "gemv" in k]
+    dom = max(gemv, key=lambda k: fetch[k][0])  # gate/up reads two matrices per expert
+    fb = fetch[dom][0] * 1024.0 * f_fetch
+    wb = write[dom][0] * 1024.0 * f_write
+    d = {"kernel": dom, "command": cmd, "calib_copy_MiB": calib_mb,
+         "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
+         "fetch_kib_per_dispatch": round(fetch[dom][0], 1), "write_kib_per_dispatch": round(write[dom][0], 1),
+         "dispatches": fetch[dom][1], "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
+         "hbm_bytes_per_launch": int(fb + wb), "kernel_source_sha256_16": kernel_source_hash(),
+         "all_kernels_fetch_kib": {k: round(v[0], 1) for k, v in fetch.items()},
+         "all_kernels_write_kib": {k: round(v[0], 1) for k, v in write.items()}}
+    with open(out, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,7 +325,21 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-mb", type=int, default=1024,
+                    help="MiB moved by the copy kernel that calibrates byte counters (0: skip)")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="write a short text summary of a rocprofv3 --stats kernel table and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic summary and exit")
+    ap.add_argument("--cmd", type=str, default="", help="the command that produced the profiler output")
     args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.calib_mb, args.cmd)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's sharding across GPUs "
@@ -239,6 +347,10 @@ def main():
         sys.exit(2)
 
     import synth
+    copy_gbs = None
+    if args.calib_mb > 0:
+        copy_gbs = copy_bandwidth(args.calib_mb, 5)
+        log(f"copy kernel ({args.calib_mb} MiB): {copy_gbs:.0f} GB/s read+write")
     wl0 = synth.WORKLOADS[args.config]
     Ts = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl0["tokens"])
     stack = Stack(args.config, args.layers, args.wbits)
@@ -286,8 +398,10 @@ def main():
                    "stacked_layers": stack.L, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<gate/up>", "bytes_per_launch": int(head["gateup_bytes"]),
-                     "avg_launch_us": round(head["stage_ms"][DOMINANT_STAGE] * 1e3, 2)},
+                     "kernel": "gemv_fast_kernel (gate/up, fused SiLU*up + Q8_0)",
+                     "bytes_per_launch": int(head["gateup_bytes"]),
+                     "avg_launch_us": round(head["stage_ms"][DOMINANT_STAGE] * 1e3, 2),
+                     "measured_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1)},
         "cpu_baseline": cpu,
         "sweep": [{"T": r["T"], "tokens_per_s": round(r["tok_s"], 1), "us_per_step": round(r["ms"] * 1e3, 2),
                    "U_mean": r["U_mean"], "gate_up_GBps": round(r["gateup_gbs"], 1),

@@ -6,7 +6,8 @@ library is not built, importing any entry point raises.
 
 Entry points (same names as the C ABI in include/coli_moe.h):
     quantize_q8_0, route, group, ffn, layer, layer_profiled,
-    blob_bytes, workspace_bytes, num_stages, stage_name, strerror.
+    blob_bytes, workspace_bytes, num_stages, stage_name, strerror;
+plus TimingEvents (HIP events for layer_profiled) and alloc_workspace.
 Tensors must be CUDA tensors, contiguous, with the dtypes documented in the header.
 """
 from __future__ import annotations
@@ -199,15 +200,61 @@ def layer(cfg: Cfg, w: Weights, x, out, workspace, topk_idx=None, topk_w=None, s
            "coli_moe_layer")
 
 
+class TimingEvents:
+    """HIP events for stage timing, created with hipEventDisableSystemFence so that
+    recording one does not write back and invalidate the caches (which would add
+    microseconds to the stage it closes). Pass to layer_profiled; read with
+    elapsed_ms(i, j) after synchronising the stream."""
+
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import torch  # noqa: F401  (loads the HIP runtime this process already uses)
+        self._hip = C.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.events = []
+        for _ in range(n):
+            ev = C.c_void_p()
+            rc = self._hip.hipEventCreateWithFlags(C.byref(ev), self._DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.events.append(ev)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = C.c_float()
+        rc = self._hip.hipEventElapsedTime(C.byref(ms), self.events[i], self.events[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self._hip.hipEventDestroy(ev)
+        self.events = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def layer_profiled(cfg: Cfg, w: Weights, x, out, workspace, events, stream=None):
-    """events: list of num_stages()+1 torch.cuda.Event(enable_timing=True)."""
+    """events: a TimingEvents(num_stages() + 1), or a list of num_stages()+1
+    torch.cuda.Event(enable_timing=True)."""
     import torch
     _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out")
-    for e in events:  # torch creates the HIP event lazily, on its first record
-        if e.cuda_event == 0:
-            e.record(stream if stream is not None else torch.cuda.current_stream(x.device))
-    arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+    if isinstance(events, TimingEvents):
+        handles = [e.value for e in events.events]
+    else:
+        for e in events:  # torch creates the HIP event lazily, on its first record
+            if e.cuda_event == 0:
+                e.record(stream if stream is not None else torch.cuda.current_stream(x.device))
+        handles = [e.cuda_event for e in events]
+    arr = (C.c_void_p * len(handles))(*[C.c_void_p(h) for h in handles])
     wc = w.c()
     _check(lib().coli_moe_layer_profiled(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out),
-                                         _ptr(workspace), workspace.numel(), _stream(stream, x), arr, len(events)),
+                                         _ptr(workspace), workspace.numel(), _stream(stream, x), arr, len(handles)),
            "coli_moe_layer_profiled")

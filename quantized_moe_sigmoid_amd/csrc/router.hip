@@ -18,9 +18,9 @@
 //     x staged in LDS; every lane issues all its weight loads before the barrier;
 //     the 2 x T fp64 partial sums of a wavefront are folded with a reduce-scatter.
 //   logits_kernel (larger T): LDS-tiled fp64 GEMM, K-split.
-//   select_kernel: one wavefront per token sums the K-split partials in a fixed
-//     order (deterministic), quantises the token's x, and performs the
-//     group-limited top-k with shuffles.
+//   select_kernel: one workgroup per token quantises the token's x (Q8_0), sums
+//     the K-split partials in a fixed order (deterministic) and performs the
+//     group-limited top-k as rank computations over LDS.
 #include "q8_0_impl.h"
 
 namespace coli {
@@ -157,21 +157,6 @@ __global__ __launch_bounds__(256) void logits_kernel(const float *__restrict__ x
 }
 
 // ------------------------------------------------------------------ selection
-// Arg-max over the wavefront of (v, i), larger v first, then lower i; carries s.
-__device__ __forceinline__ void wave_argmax(double &v, int &i, double &s) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const double ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    const double os = __shfl_xor(s, o);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-      s = os;
-    }
-  }
-}
-
 struct SelectArgs {
   const double *part;
   int ksplit, T, E, G, Gk, k;
@@ -185,103 +170,115 @@ struct SelectArgs {
   int2 *xds;
 };
 
-template <int EPL>
-__device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane) {
-  const int E = a.E, G = a.G, k = a.k;
-  const int m = E / G;
-  const double NEG = -INFINITY;
-  double s[EPL], c[EPL];
+constexpr int SEL_NT = 256;  // threads per token
+
+// (v, i) ranks before (v2, i2): larger value first, then lower index
+__device__ __forceinline__ bool before(double v2, int i2, double v, int i) { return v2 > v || (v2 == v && i2 < i); }
+
+// One workgroup per token. Every step is a rank computation over LDS, so the
+// selection costs a few passes over E values instead of k dependent arg-max
+// reductions:
+//   c_e in LDS; the rank of e inside its group (among c, lower index first) puts
+//   the two best values of each group in place; the group score is their sum;
+//   the rank of a group among the group scores decides whether it is kept;
+//   experts of dropped groups get c = -inf; the rank of e among all c is its
+//   output slot when below k. Ranks are exact (no ties: the index breaks them).
+// The token's row of x is quantised (Q8_0) first, by the whole workgroup.
+template <int EPT>
+__global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
+  __shared__ double cs[SEL_NT * EPT];
+  __shared__ double gtop[64][2];
+  __shared__ double gsc[64];
+  __shared__ int gkeep[64];
+  __shared__ int sel_e[64];
+  __shared__ double sel_s[64];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int E = a.E, G = a.G, k = a.k, m = E / G;
+
+  if (a.xq) {  // eight lanes per 32-value block
+    const int nblk = a.H / QK;
+    const float *xr = a.x + (int64_t)t * a.H;
+    for (int b0 = 0; b0 < nblk; b0 += SEL_NT / 8) {
+      const int blk = b0 + (tid >> 3), sub = tid & 7;
+      const bool valid = blk < nblk;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (valid) v = reinterpret_cast<const float4 *>(xr)[blk * 8 + sub];
+      uint32_t packed;
+      int sum;
+      const float d = q8_0_block8(v, packed, sum);
+      if (valid) {
+        reinterpret_cast<uint32_t *>(a.xq + (int64_t)t * a.H)[blk * 8 + sub] = packed;
+        if (sub == 0) a.xds[(int64_t)t * nblk + blk] = make_int2(__float_as_int(d), sum);
+      }
+    }
+  }
+
+  double s[EPT], c[EPT];
 #pragma unroll
-  for (int i = 0; i < EPL; i++) {
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
     s[i] = 0.0;
-    c[i] = NEG;
-    const int e = lane * EPL + i;
+    c[i] = -INFINITY;
     if (e < E) {
       double z = 0.0;
-#pragma unroll 8
       for (int ks = 0; ks < a.ksplit; ks++) z += a.part[((int64_t)ks * a.T + t) * E + e];
       s[i] = 1.0 / (1.0 + exp(-z));
       c[i] = s[i] + (double)a.bias[e];
+      cs[e] = c[i];
     }
   }
-  // group scores; lane g keeps the score of group g
-  double my_gs = NEG;
-  for (int g = 0; g < G; g++) {
-    const int lo = g * m, hi = lo + m;
-    double v1 = NEG, dummy = 0.0;
-    int i1 = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-      const int e = lane * EPL + i;
-      if (e >= lo && e < hi && (c[i] > v1 || (c[i] == v1 && e < i1))) {
-        v1 = c[i];
-        i1 = e;
-      }
-    }
-    wave_argmax(v1, i1, dummy);
-    double gs = v1;
-    if (m > 1) {
-      double v2 = NEG;
-      int i2 = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; i++) {
-        const int e = lane * EPL + i;
-        if (e >= lo && e < hi && e != i1 && (c[i] > v2 || (c[i] == v2 && e < i2))) {
-          v2 = c[i];
-          i2 = e;
-        }
-      }
-      wave_argmax(v2, i2, dummy);
-      gs = v1 + v2;
-    }
-    if (lane == g) my_gs = gs;
-  }
-  uint64_t kept = 0;
-  for (int r = 0; r < a.Gk; r++) {
-    const bool cand = lane < G && !((kept >> lane) & 1ull);
-    double v = cand ? my_gs : NEG, dummy = 0.0;
-    int gi = cand ? lane : 0x7fffffff;
-    wave_argmax(v, gi, dummy);
-    kept |= 1ull << gi;
-  }
-  uint32_t taken = 0;
-  double my_s = 0.0;
-  int my_e = 0;
-  for (int j = 0; j < k; j++) {
-    double v = NEG, sv = 0.0;
-    int ei = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-      const int e = lane * EPL + i;
-      if (e < E && ((kept >> (e / m)) & 1ull) && !((taken >> i) & 1u) && (c[i] > v || (c[i] == v && e < ei))) {
-        v = c[i];
-        ei = e;
-        sv = s[i];
-      }
-    }
-    wave_argmax(v, ei, sv);
-    if (ei / EPL == lane) taken |= 1u << (ei - lane * EPL);
-    if (lane == j) {
-      my_s = sv;
-      my_e = ei;
-    }
-  }
-  double S = 0.0;
-  for (int j = 0; j < k; j++) S += __shfl(my_s, j);
-  if (lane < k) {
-    a.idx[(int64_t)t * k + lane] = my_e;
-    a.w[(int64_t)t * k + lane] = (float)((my_s / S) * (double)a.rsf);
-  }
-}
+  if (tid < 64) sel_e[tid] = -1;
+  __syncthreads();
 
-// One wavefront per token, four tokens per workgroup.
-template <int EPL>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  if (a.xq) q8_0_row_wave(a.x + (int64_t)t * a.H, a.H, a.xq + (int64_t)t * a.H, a.xds + (int64_t)t * (a.H / QK), lane);
-  select_token<EPL>(a, t, lane);
+  // the two best c of each group
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
+    if (e < E) {
+      const int lo = (e / m) * m;
+      int r = 0;
+      for (int e2 = lo; e2 < lo + m; e2++) r += before(cs[e2], e2, c[i], e) ? 1 : 0;
+      if (r < 2) gtop[e / m][r] = c[i];
+    }
+  }
+  __syncthreads();
+  if (tid < G) gsc[tid] = (m > 1) ? gtop[tid][0] + gtop[tid][1] : gtop[tid][0];
+  __syncthreads();
+  if (tid < G) {
+    int r = 0;
+    for (int g2 = 0; g2 < G; g2++) r += before(gsc[g2], g2, gsc[tid], tid) ? 1 : 0;
+    gkeep[tid] = r < a.Gk;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
+    if (e < E && !gkeep[e / m]) {
+      c[i] = -INFINITY;
+      cs[e] = -INFINITY;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
+    if (e < E && c[i] != -INFINITY) {
+      int r = 0;
+      for (int e2 = 0; e2 < E; e2++) r += before(cs[e2], e2, c[i], e) ? 1 : 0;
+      if (r < k) {
+        sel_e[r] = e;
+        sel_s[r] = s[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    double S = 0.0;
+    for (int j = 0; j < k; j++) S += sel_s[j];
+    const int e = sel_e[tid];
+    a.idx[(int64_t)t * k + tid] = e;
+    a.w[(int64_t)t * k + tid] = (e >= 0) ? (float)((sel_s[tid] / S) * (double)a.rsf) : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -330,22 +327,13 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.H = H;
   a.xq = r.xq;
   a.xds = r.xds;
-  const int epl = (E + 63) / 64;
-#define COLI_SEL(EPLV) hipLaunchKernelGGL((select_kernel<EPLV>), dim3((T + 3) / 4), dim3(256), 0, s, a)
-#define COLI_SEL_Q(EPLV) COLI_SEL(EPLV);
-  if (epl <= 1) {
-    COLI_SEL_Q(1)
-  } else if (epl <= 2) {
-    COLI_SEL_Q(2)
-  } else if (epl <= 4) {
-    COLI_SEL_Q(4)
-  } else if (epl <= 8) {
-    COLI_SEL_Q(8)
-  } else {
-    COLI_SEL_Q(16)
-  }
-#undef COLI_SEL_Q
-#undef COLI_SEL
+  if (T == 0) return hipSuccess;
+  if (E <= SEL_NT)
+    hipLaunchKernelGGL(select_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a);
+  else if (E <= 2 * SEL_NT)
+    hipLaunchKernelGGL(select_kernel<2>, dim3(T), dim3(SEL_NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(select_kernel<4>, dim3(T), dim3(SEL_NT), 0, s, a);
   return hipGetLastError();
 }
 

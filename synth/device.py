@@ -34,6 +34,8 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.coli_synth_fill_blobs.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]
         L.coli_synth_fill_blobs.restype = C.c_int
+        L.coli_synth_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+        L.coli_synth_copy.restype = C.c_int
         _lib = L
     return _lib
 
@@ -54,3 +56,17 @@ def fill_blobs(out, seed: int, layer: int, first_expert: int, n_blobs: int, blob
     if rc != 0:
         raise RuntimeError(f"coli_synth_fill_blobs failed: {rc}")
     torch.cuda.current_stream(out.device).synchronize()  # keys tensor lifetime
+
+
+def copy(src, dst, stream=None):
+    """Streaming device copy of ``src`` into ``dst`` (same byte size, multiple of 16):
+    the reference kernel of known traffic for scaling hardware byte counters."""
+    import torch
+
+    assert src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()
+    nbytes = src.numel() * src.element_size()
+    assert nbytes == dst.numel() * dst.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(src.device)
+    rc = lib().coli_synth_copy(C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()), nbytes, C.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"coli_synth_copy failed: {rc}")

@@ -39,7 +39,23 @@ __global__ void fill_blobs_kernel(uint64_t *__restrict__ out, const uint64_t *__
   }
 }
 
+// Plain streaming copy of n16 16-byte words: a kernel whose HBM traffic is known
+// exactly (n16 * 16 bytes read, the same written), run beside the MoE kernels so
+// that hardware byte counters can be scaled to bytes.
+__global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16) {
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n16; g += (int64_t)gridDim.x * blockDim.x)
+    dst[g] = src[g];
+}
+
 }  // namespace
+
+extern "C" int coli_synth_copy(const void *src, void *dst, int64_t bytes, void *stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16) return -1;
+  if (((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0) return -4;
+  hipLaunchKernelGGL(copy_kernel, dim3(2048), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int coli_synth_fill_blobs(void *out, const void *keys_dev, int64_t blob_bytes, int32_t n_blobs,
                                      int32_t wbits, void *stream) {
