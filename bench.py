@@ -318,7 +318,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--wbits", type=int, default=None)
     ap.add_argument("--tokens", type=str, default=None, help="comma list of T; the last is the headline")
     ap.add_argument("--layers", type=int, default=8)

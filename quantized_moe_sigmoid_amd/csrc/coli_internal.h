@@ -20,7 +20,7 @@ __host__ __device__ inline int64_t row_bytes(int wfmt, int n) { return (int64_t)
 
 struct WsLayout {
   // byte offsets into the workspace (all 256-byte aligned)
-  size_t xq, xds, hq, hds, ypair, logits, idx, w, cnt, off, perm, active, nact, total;
+  size_t xq, xds, hq, hds, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, total;
 };
 
 // Workspace layout for T tokens (valid cfg assumed).
@@ -70,6 +70,13 @@ struct FfnArgs {
 };
 hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s);
 hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s);
+// grouped-GEMM (MFMA) path for batches whose experts see many tokens
+int32_t mfma_gmax(int32_t T, int32_t k, int32_t E, int32_t has_shared);  // token-tile capacity
+hipError_t launch_plan(const FfnArgs &a, int4 *tiles, int32_t *ntiles, int32_t gmax, hipStream_t s);
+hipError_t launch_mfma_gateup(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
+                              hipStream_t s);
+hipError_t launch_mfma_down(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
+                            hipStream_t s);
 hipError_t launch_combine(const float *ypair, const float *w, int32_t T, int32_t k, int32_t H,
                           int32_t has_shared, float *out, hipStream_t s);
 

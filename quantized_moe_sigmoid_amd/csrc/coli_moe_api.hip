@@ -27,6 +27,8 @@ WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit) {
   L.perm = o;   o = align256(o + P * sizeof(int32_t));
   L.active = o; o = align256(o + E * sizeof(int32_t));
   L.nact = o;   o = align256(o + sizeof(int32_t));
+  L.tiles = o;  o = align256(o + (size_t)mfma_gmax(T, c.top_k, c.n_experts, c.has_shared) * sizeof(int4));
+  L.ntiles = o; o = align256(o + sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -114,10 +116,17 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.hq = at<int8_t>(ws, L.hq);
   a.hds = at<int2>(ws, L.hds);
   a.ypair = at<float>(ws, L.ypair);
+  // Batches past the decode size run the expert FFNs as grouped GEMMs on the
+  // matrix cores; a tile plan of the union comes first.
+  const bool gemm = local_idx == nullptr && (int64_t)T * c.top_k > LOCAL_GROUP_MAX_P;
+  const int32_t gmax = mfma_gmax(T, c.top_k, c.n_experts, c.has_shared);
+  int4 *tiles = at<int4>(ws, L.tiles);
+  int32_t *ntiles = at<int32_t>(ws, L.ntiles);
+  if (gemm && (st = dev(launch_plan(a, tiles, ntiles, gmax, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[1], s)))) return st;
-  if ((st = dev(launch_gateup(c.wfmt, a, s)))) return st;
+  if ((st = dev(gemm ? launch_mfma_gateup(c.wfmt, a, tiles, ntiles, gmax, s) : launch_gateup(c.wfmt, a, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
-  if ((st = dev(launch_down(c.wfmt, a, s)))) return st;
+  if ((st = dev(gemm ? launch_mfma_down(c.wfmt, a, tiles, ntiles, gmax, s) : launch_down(c.wfmt, a, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[3], s)))) return st;
   if ((st = dev(launch_combine(a.ypair, topk_w, T, c.top_k, c.hidden, c.has_shared, out, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[4], s)))) return st;

@@ -630,12 +630,8 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
     __syncthreads();
     if (nt <= 1)
       fast_pass<WB, NMAT, LPR, CPL, WR, 1>(c, nt, lane, wv);
-    else if (nt <= 2)
+    else
       fast_pass<WB, NMAT, LPR, CPL, WR, 2>(c, nt, lane, wv);
-    else if (nt <= 4)
-      fast_pass<WB, NMAT, LPR, CPL, WR, 4>(c, nt, lane, wv);
-    else if constexpr (WB != 2)
-      fast_pass<WB, NMAT, LPR, CPL, WR, 8>(c, nt, lane, wv);
     __syncthreads();
     // epilogue over the tile's rows x nt tokens
     if constexpr (MODE == MODE_GATEUP) {
@@ -682,7 +678,10 @@ static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int 
   constexpr int TILE = 4 * WR;
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   if (nrows % TILE) return hipErrorNotSupported;
-  const int ntmax = min(WB == 2 ? 4 : 8, a.T);
+  // two tokens per pass: the accumulators of larger passes cost occupancy (2 -> 3 waves
+  // per SIMD for the int4 gate/up instantiation), which matters more than reloading a
+  // tile's weights from L2 for the rare expert with more than two tokens
+  const int ntmax = min(2, a.T);
   const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(int2) + (size_t)NMAT * 8 * TILE * sizeof(float) +
                      16 * sizeof(int);
   dim3 grid(nrows / TILE, slots_grid.y);

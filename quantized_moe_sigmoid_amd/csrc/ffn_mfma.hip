@@ -1,0 +1,402 @@
+// ffn_mfma.hip — expert FFNs of large batches (prefill, long verify) as grouped
+// GEMMs on the int8 matrix cores of gfx950 (v_mfma_i32_32x32x32_i8).
+//
+// Batch-union (colibri-strix README, "What's implemented", batch-union item): each
+// expert of the union is one GEMM of its weight rows against the Q8_0 rows of the
+// tokens routed to it, the weights dequantised on use (same section, quantization
+// kernels item) and multiplied with integer dots (integer-dot kernels item).
+//
+// One MFMA of 32 x 32 x 32 covers exactly one Q8_0 block along K, so its int32
+// results are the exact block dots I_b of 32 weight rows x 32 tokens. Each lane's
+// outputs belong to one token (the MFMA column), so scaling by that token's block
+// scale is one fp32 multiply-add per result: acc += d_b * I_b. The K order inside
+// a block is free (the block is reduced whole), which is what makes the packed
+// layouts cheap to feed: lanes 0-31 take the first 16 values of a block, lanes
+// 32-63 the last 16, i.e. the low resp. high nibbles of an int4 block.
+//
+// Work: a workgroup (4 wavefronts, 2 x 2) owns 64 weight rows x 64 tokens of one
+// expert; a wavefront 32 rows x 32 tokens (gate and up together in the gate/up
+// pass). Token tiles of the union are listed by plan_kernel; the 1-D grid is
+// remapped so that the token tiles of one (expert, row tile) land on one XCD in
+// consecutive order and share its L2 copy of the weight rows.
+#include "coli_internal.h"
+
+namespace coli {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int MF_ROWS = 64;  // weight rows per workgroup
+constexpr int MF_TOK = 64;   // tokens per workgroup (one token tile)
+constexpr int MF_KC = 4;     // Q8_0 blocks per K stage staged through LDS
+
+// ------------------------------------------------------------------ plan
+// Token tiles of the union, in slot order (shared expert first, then the experts of
+// `active`): tiles[g] = {expert, first perm index (-1: shared expert), tokens of the
+// expert, tile index}. *ntiles = number of tiles.
+__global__ __launch_bounds__(1024) void plan_kernel(FfnArgs a, int4 *__restrict__ tiles, int32_t *__restrict__ ntiles,
+                                                    int gmax) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int hs = a.has_shared;
+  const int na = max(0, min(*a.nact, a.E));
+  const int ns = hs + na;
+  // two slots per thread: u0 = 2 * tid, u0 + 1
+  int e[2], beg[2], n[2], nt[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int u = 2 * tid + q;
+    e[q] = 0;
+    beg[q] = 0;
+    n[q] = 0;
+    if (u < ns) {
+      if (hs && u == 0) {
+        e[q] = a.E;
+        beg[q] = -1;
+        n[q] = a.T;
+      } else {
+        const int ex = a.active[u - hs];
+        e[q] = ex;
+        beg[q] = a.off[ex];
+        n[q] = a.off[ex + 1] - beg[q];
+      }
+    }
+    nt[q] = (n[q] + MF_TOK - 1) / MF_TOK;
+  }
+  const int mine = nt[0] + nt[1];
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int i = 0; i < 16; i++) {
+    if (i < wv) base += wsum[i];
+    total += wsum[i];
+  }
+  int g = base + incl - mine;
+#pragma unroll
+  for (int q = 0; q < 2; q++)
+    for (int t = 0; t < nt[q]; t++, g++)
+      if (g < gmax) tiles[g] = make_int4(e[q], beg[q], n[q], t);
+  if (tid == 0) *ntiles = min(total, gmax);
+}
+
+// ------------------------------------------------------------------ staging
+// Per-byte sign extension of b-bit two's complement fields already isolated in
+// each byte: flip the sign bit to offset binary, add 0x80 - 2^(b-1), flip bit 7.
+// No byte carries into the next (every byte stays <= 0x80 + 2^(b-1) - 1).
+template <int BITS>
+__device__ __forceinline__ uint32_t sext_bytes(uint32_t t) {
+  constexpr uint32_t SGN = (BITS == 4) ? 0x08080808u : 0x02020202u;
+  constexpr uint32_t ADD = (BITS == 4) ? 0x78787878u : 0x7E7E7E7Eu;
+  return ((t ^ SGN) + ADD) ^ 0x80808080u;
+}
+
+// LDS tiles of one K stage of KC blocks, int8 in natural K order; rows padded by
+// 16 bytes against bank conflicts.
+template <int NMAT, int KC>
+struct MfLds {
+  static constexpr int ROWB = KC * QK + 16;  // bytes per row (and per token)
+  int8_t a[2][NMAT][MF_ROWS][ROWB];
+  int8_t b[2][MF_TOK][ROWB];
+  float d[2][MF_TOK][KC];
+};
+
+enum { MF_GATEUP = 0, MF_DOWN = 1 };
+
+// Global -> register part of one stage: the lane's share of the packed weight
+// rows, of the token rows and of the block scales.
+template <int WB, int NMAT, int KC>
+struct MfRegs {
+  // weight bytes per (matrix, row) and stage: KC * 32 * WB / 8; 16-byte pieces per row
+  static constexpr int APIECES = KC * QK * WB / 8 / 16;
+  static constexpr int ATOTAL = NMAT * MF_ROWS * APIECES;
+  static constexpr int ALOADS = (ATOTAL + 255) / 256;  // per thread (the last may be partial)
+  static constexpr int BLOADS = MF_TOK * KC * QK / 16 / 256;
+  uint4 a[ALOADS];
+  uint4 b[BLOADS];
+  float d;
+};
+
+// ------------------------------------------------------------------ GEMM
+template <int WB, int MODE, int KC>
+__global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__restrict__ tiles,
+                                                   const int32_t *__restrict__ ntiles, int gmax, int nf) {
+  constexpr int NMAT = (MODE == MF_GATEUP) ? 2 : 1;
+  using Lds = MfLds<NMAT, KC>;
+  using Regs = MfRegs<WB, NMAT, KC>;
+  constexpr int ROWB = Lds::ROWB;
+  constexpr int APIECES = Regs::APIECES;
+  constexpr int ATOTAL = Regs::ATOTAL;
+  static_assert(ATOTAL % 64 == 0, "weight pieces: whole wavefronts");
+  static_assert(Regs::BLOADS >= 1 && MF_TOK * KC * 2 % 256 == 0, "token pieces per thread");
+  static_assert(MF_TOK * KC == 256, "one block scale per thread and stage");
+  __shared__ Lds L;
+  __shared__ int act_rows[MF_TOK];
+
+  // XCD-aware order: hardware workgroup i runs on XCD i % 8; give each XCD one
+  // contiguous range of work (token tiles fastest), so the tiles of one (expert,
+  // row tile) run on one XCD one after the other and share its L2
+  const int nwork = nf * gmax;  // a multiple of 8
+  const int bid = blockIdx.x;
+  const int w = (bid & 7) * (nwork >> 3) + (bid >> 3);
+  const int ft = w / gmax, g = w % gmax;
+  if (g >= *ntiles) return;
+  const int4 ti = tiles[g];  // expert, first perm index (-1: shared), tokens, tile
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int grp = lane >> 5, li = lane & 31;
+  const int K = (MODE == MF_GATEUP) ? a.H : a.F;
+  const int nkb = K / QK;
+  const int P = a.T * a.k;
+  const int64_t rb = row_bytes(WB, K);
+  const int64_t rbh = row_bytes(WB, a.H);
+  const uint8_t *blob = a.experts + (int64_t)ti.x * a.blob_bytes;
+  const uint8_t *mat0 = (MODE == MF_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+  const uint8_t *mat1 = blob + (int64_t)a.F * rbh;
+  const int r0 = ft * MF_ROWS;
+
+  // token rows of the tile: activation row and output row; past the expert's
+  // tokens the tile repeats its first token and writes nothing
+  if (tid < MF_TOK) {
+    const int i = ti.w * MF_TOK + tid;
+    const int ic = i < ti.z ? i : ti.w * MF_TOK;
+    int act;
+    if (ti.y < 0) act = (MODE == MF_GATEUP) ? ic : P + ic;
+    else {
+      const int p = a.perm[ti.y + ic];
+      act = (MODE == MF_GATEUP) ? p / a.k : p;
+    }
+    act_rows[tid] = act;
+  }
+  __syncthreads();
+  const int8_t *asrc = (MODE == MF_GATEUP) ? a.xq : a.hq;
+  const int2 *dsrc = (MODE == MF_GATEUP) ? a.xds : a.hds;
+  // this thread's token pieces: piece q -> token q / (2 KC), 16-byte part q % (2 KC)
+  int64_t boff[Regs::BLOADS];
+#pragma unroll
+  for (int j = 0; j < Regs::BLOADS; j++) {
+    const int q = tid + 256 * j;
+    boff[j] = (int64_t)act_rows[q / (2 * KC)] * K + (q % (2 * KC)) * 16;
+  }
+  const int64_t doff = (int64_t)act_rows[tid / KC] * nkb + tid % KC;
+
+  auto gload = [&](int s, Regs &r) {
+    const int kb0 = s * KC;  // first block of the stage
+#pragma unroll
+    for (int j = 0; j < Regs::ALOADS; j++) {
+      const int q = tid + 256 * j;
+      if (ATOTAL % 256 != 0 && q >= ATOTAL) break;
+      const int m = q / (MF_ROWS * APIECES), row = (q / APIECES) % MF_ROWS, pc = q % APIECES;
+      const uint8_t *base = (NMAT == 2 && m == 1) ? mat1 : mat0;
+      r.a[j] = *reinterpret_cast<const uint4 *>(base + (int64_t)(r0 + row) * rb + (int64_t)kb0 * (QK * WB / 8) + pc * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < Regs::BLOADS; j++)
+      r.b[j] = *reinterpret_cast<const uint4 *>(asrc + boff[j] + (int64_t)kb0 * QK);
+    r.d = __int_as_float(dsrc[doff + kb0].x);
+  };
+
+  auto lstore = [&](int buf, const Regs &r) {
+#pragma unroll
+    for (int j = 0; j < Regs::ALOADS; j++) {
+      const int q = tid + 256 * j;
+      if (ATOTAL % 256 != 0 && q >= ATOTAL) break;
+      const int m = q / (MF_ROWS * APIECES), row = (q / APIECES) % MF_ROWS, pc = q % APIECES;
+      int8_t *dst = &L.a[buf][m][row][0];
+      const uint4 v = r.a[j];
+      if constexpr (WB == 8) {
+        *reinterpret_cast<uint4 *>(dst + pc * 16) = v;
+      } else if constexpr (WB == 4) {
+        // one 16-byte block: values 0..15 in the low nibbles, 16..31 in the high ones
+        uint4 lo, hi;
+        lo.x = sext_bytes<4>(v.x & 0x0F0F0F0Fu);
+        lo.y = sext_bytes<4>(v.y & 0x0F0F0F0Fu);
+        lo.z = sext_bytes<4>(v.z & 0x0F0F0F0Fu);
+        lo.w = sext_bytes<4>(v.w & 0x0F0F0F0Fu);
+        hi.x = sext_bytes<4>((v.x >> 4) & 0x0F0F0F0Fu);
+        hi.y = sext_bytes<4>((v.y >> 4) & 0x0F0F0F0Fu);
+        hi.z = sext_bytes<4>((v.z >> 4) & 0x0F0F0F0Fu);
+        hi.w = sext_bytes<4>((v.w >> 4) & 0x0F0F0F0Fu);
+        *reinterpret_cast<uint4 *>(dst + pc * 32) = lo;
+        *reinterpret_cast<uint4 *>(dst + pc * 32 + 16) = hi;
+      } else {
+        // two 8-byte blocks; byte j holds values j + 8m in bits 2m (m = 0..3)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const uint32_t w0 = h ? v.z : v.x, w1 = h ? v.w : v.y;
+          uint4 o0, o1;
+          o0.x = sext_bytes<2>(w0 & 0x03030303u);
+          o0.y = sext_bytes<2>(w1 & 0x03030303u);
+          o0.z = sext_bytes<2>((w0 >> 2) & 0x03030303u);
+          o0.w = sext_bytes<2>((w1 >> 2) & 0x03030303u);
+          o1.x = sext_bytes<2>((w0 >> 4) & 0x03030303u);
+          o1.y = sext_bytes<2>((w1 >> 4) & 0x03030303u);
+          o1.z = sext_bytes<2>((w0 >> 6) & 0x03030303u);
+          o1.w = sext_bytes<2>((w1 >> 6) & 0x03030303u);
+          *reinterpret_cast<uint4 *>(dst + pc * 64 + h * 32) = o0;
+          *reinterpret_cast<uint4 *>(dst + pc * 64 + h * 32 + 16) = o1;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < Regs::BLOADS; j++) {
+      const int q = tid + 256 * j;
+      *reinterpret_cast<uint4 *>(&L.b[buf][q / (2 * KC)][(q % (2 * KC)) * 16]) = r.b[j];
+    }
+    L.d[buf][tid / KC][tid % KC] = r.d;
+  };
+
+  float acc[NMAT][16];
+#pragma unroll
+  for (int m = 0; m < NMAT; m++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[m][r] = 0.0f;
+
+  // one stage from LDS: per block, an exact int32 block dot by MFMA, then the scale
+  auto compute = [&](int buf) {
+    const int8_t *arow0 = &L.a[buf][0][wm * 32 + li][16 * grp];
+    const int8_t *brow = &L.b[buf][wn * 32 + li][16 * grp];
+#pragma unroll
+    for (int kb = 0; kb < KC; kb++) {
+      const v4i bv = *reinterpret_cast<const v4i *>(brow + kb * QK);
+      const float d = L.d[buf][wn * 32 + li][kb];
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) {
+        const v4i av = *reinterpret_cast<const v4i *>(arow0 + m * (MF_ROWS * ROWB) + kb * QK);
+        const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[m][r] += d * (float)I[r];
+      }
+    }
+  };
+
+  const int ns = nkb / KC;
+  {
+    Regs r;
+    gload(0, r);
+    lstore(0, r);
+  }
+  __syncthreads();
+  for (int s = 0; s < ns; s++) {
+    Regs r;
+    const bool more = s + 1 < ns;
+    if (more) gload(s + 1, r);
+    compute(s & 1);
+    if (more) lstore((s + 1) & 1, r);
+    __syncthreads();
+  }
+
+  // epilogue. Result r of this lane: row r0 + 32 wm + 8 (r / 4) + 4 grp + r % 4,
+  // token wn * 32 + li of the tile.
+  const int i = ti.w * MF_TOK + wn * 32 + li;
+  const bool valid = i < ti.z;
+  int out_row = 0;
+  if (valid) out_row = (ti.y < 0) ? P + i : a.perm[ti.y + i];
+  const int rbase = r0 + wm * 32;
+  const float *sc = a.scales + (int64_t)ti.x * (2 * a.F + a.H);
+  if constexpr (MODE == MF_GATEUP) {
+    float h[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int f = rbase + 8 * (r >> 2) + 4 * grp + (r & 3);
+      const float gv = sc[f] * acc[0][r];
+      const float uv = sc[a.F + f] * acc[1][r];
+      h[r] = (gv / (1.0f + expf(-gv))) * uv;
+      amax = fmaxf(amax, fabsf(h[r]));
+    }
+    // the 32 rows of this Q8_0 block of h sit in lanes li and li + 32
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float d = amax / 127.0f;
+    int sum = 0;
+    uint32_t packed[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        int q = 0;
+        if (d != 0.0f) q = (int)fminf(fmaxf(roundf(h[4 * rr + j] / d), -127.0f), 127.0f);
+        sum += q;
+        pk |= (uint32_t)(q & 0xFF) << (8 * j);
+      }
+      packed[rr] = pk;
+    }
+    sum += __shfl_xor(sum, 32);
+    if (valid) {
+      int8_t *hrow = a.hq + (int64_t)out_row * a.F + rbase + 4 * grp;
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) *reinterpret_cast<uint32_t *>(hrow + 8 * rr) = packed[rr];
+      if (grp == 0) a.hds[(int64_t)out_row * (a.F / QK) + rbase / QK] = make_int2(__float_as_int(d), sum);
+    }
+  } else {
+    if (valid) {
+      const float *sd = sc + 2 * a.F;
+      float *yrow = a.ypair + (int64_t)out_row * a.H + rbase + 4 * grp;
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        const int f = rbase + 8 * rr + 4 * grp;
+        float4 v;
+        v.x = sd[f] * acc[0][4 * rr];
+        v.y = sd[f + 1] * acc[0][4 * rr + 1];
+        v.z = sd[f + 2] * acc[0][4 * rr + 2];
+        v.w = sd[f + 3] * acc[0][4 * rr + 3];
+        *reinterpret_cast<float4 *>(yrow + 8 * rr) = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+int32_t mfma_gmax(int32_t T, int32_t k, int32_t E, int32_t has_shared) {
+  const int64_t rows = (int64_t)T * k + (int64_t)has_shared * T;
+  const int64_t g = (rows + MF_TOK - 1) / MF_TOK + E + has_shared;
+  return (int32_t)((g + 7) / 8 * 8);
+}
+
+hipError_t launch_plan(const FfnArgs &a, int4 *tiles, int32_t *ntiles, int32_t gmax, hipStream_t s) {
+  if (a.E + a.has_shared > 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, tiles, ntiles, gmax);
+  return hipGetLastError();
+}
+
+template <int WB, int MODE>
+static hipError_t launch_mf(const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax, hipStream_t s) {
+  const int rows = (MODE == MF_GATEUP) ? a.F : a.H;
+  const int K = (MODE == MF_GATEUP) ? a.H : a.F;
+  if (rows % MF_ROWS || K % (MF_KC * QK) || gmax % 8) return hipErrorInvalidValue;
+  const int nf = rows / MF_ROWS;
+  const int64_t nwork = (int64_t)nf * gmax;
+  if (nwork > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles, gmax, nf);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_gateup(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
+                              hipStream_t s) {
+  switch (wfmt) {
+    case 4: return launch_mf<4, MF_GATEUP>(a, tiles, ntiles, gmax, s);
+    case 8: return launch_mf<8, MF_GATEUP>(a, tiles, ntiles, gmax, s);
+    case 2: return launch_mf<2, MF_GATEUP>(a, tiles, ntiles, gmax, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_down(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
+                            hipStream_t s) {
+  switch (wfmt) {
+    case 4: return launch_mf<4, MF_DOWN>(a, tiles, ntiles, gmax, s);
+    case 8: return launch_mf<8, MF_DOWN>(a, tiles, ntiles, gmax, s);
+    case 2: return launch_mf<2, MF_DOWN>(a, tiles, ntiles, gmax, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace coli

@@ -189,6 +189,14 @@ LAYER_CASES = [  # cfg kwargs, T, seed
     (_cfg(hidden=640, ffn=384, n_experts=12, top_k=2, has_shared=True), 1, 16),
     (_cfg(hidden=2048, ffn=1024, n_experts=64, top_k=8), 16, 17),
     (_cfg(hidden=256, ffn=128, n_experts=4, top_k=4), 29, 18),   # every expert gets many tokens
+    # more than 512 (token, expert) pairs: the grouped-GEMM (MFMA) path, ragged token tiles
+    (_cfg(hidden=256, ffn=128, n_experts=16, top_k=4), 160, 19),
+    (_cfg(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, rsf=2.5, has_shared=True), 131, 20),
+    (_cfg(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, rsf=2.5, has_shared=True,
+          wbits=8), 117, 21),
+    (_cfg(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, rsf=2.5, has_shared=True,
+          wbits=2), 109, 22),
+    (_cfg(hidden=512, ffn=256, n_experts=8, top_k=2, has_shared=True), 300, 23),  # experts with > 64 tokens
 ]
 
 
@@ -206,11 +214,12 @@ def test_layer_vs_oracle(q, orc, cfgd, T, seed):
     assert err.max() <= TOL, err.max()
 
 
-def test_ffn_entry_matches_layer(q, orc):
-    """coli_moe_ffn on the oracle's route (grouped by coli_moe_group) equals the oracle FFN."""
+@pytest.mark.parametrize("T", [21, 150])
+def test_ffn_entry_matches_layer(q, orc, T):
+    """coli_moe_ffn on the oracle's route (grouped by coli_moe_group) equals the oracle FFN
+    (T = 150: 750 pairs, the grouped-GEMM path)."""
     import torch
     cfgd = _cfg(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, rsf=2.5, has_shared=True)
-    T = 21
     inp = synth.layer_inputs(31, 0, tokens=T, hidden=384, ffn=256, n_experts=24, has_shared=True, wbits=4)
     ocfg = orc.make_cfg(**cfgd)
     ridx, rw = orc.route(ocfg, inp["router_w"], inp["router_bias"], inp["x"])
@@ -261,9 +270,10 @@ def _exact_inputs(H, F, E, wbits, T, seed, zero_routed_down=False):
     return x, np.stack(blobs), np.stack(scales)
 
 
-@pytest.mark.parametrize("wbits", [4, 8, 2])
-def test_layer_exact_case_bitidentical(q, orc, wbits):
-    H, F, E, T = 256, 128, 6, 11
+@pytest.mark.parametrize("wbits,T", [(4, 11), (8, 11), (2, 11), (4, 530), (8, 530), (2, 530)])
+def test_layer_exact_case_bitidentical(q, orc, wbits, T):
+    """T = 530 (k = 1) takes the grouped-GEMM path."""
+    H, F, E = 256, 128, 6
     x, blobs, scales = _exact_inputs(H, F, E, wbits, T, 100 + wbits)
     cfgd = _cfg(hidden=H, ffn=F, n_experts=E, top_k=1, rsf=1.0, wbits=wbits)
     rw = synth.router_weight(3, 0, E, H, std=0.001)
@@ -276,11 +286,12 @@ def test_layer_exact_case_bitidentical(q, orc, wbits):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("wbits", [4, 8, 2])
-def test_shared_expert_exact_case_bitidentical(q, orc, wbits):
+@pytest.mark.parametrize("wbits,T", [(4, 13), (8, 13), (2, 13), (4, 181), (8, 181), (2, 181)])
+def test_shared_expert_exact_case_bitidentical(q, orc, wbits, T):
     """Routed experts with all-zero down rows contribute exact zeros, so the output is
-    the shared expert alone and must be bit-identical (k > 1, grouped router)."""
-    H, F, E, T = 256, 128, 9, 13   # 8 routed + the shared expert (the last blob)
+    the shared expert alone and must be bit-identical (k > 1, grouped router).
+    T = 181 (543 pairs) takes the grouped-GEMM path."""
+    H, F, E = 256, 128, 9   # 8 routed + the shared expert (the last blob)
     x, blobs, scales = _exact_inputs(H, F, E, wbits, T, 200 + wbits, zero_routed_down=True)
     cfgd = _cfg(hidden=H, ffn=F, n_experts=E - 1, top_k=3, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
                 wbits=wbits)
