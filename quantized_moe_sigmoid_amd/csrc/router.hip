@@ -17,7 +17,8 @@
 //   logits_decode_kernel (T <= 16): 8 experts per workgroup and one K-chunk of
 //     x staged in LDS; every lane issues all its weight loads before the barrier;
 //     the 2 x T fp64 partial sums of a wavefront are folded with a reduce-scatter.
-//   logits_kernel (larger T): LDS-tiled fp64 GEMM, K-split.
+//   logits_mfma_kernel (T > 16): fp64 MFMA GEMM, K-split; logits_kernel (T <= 16
+//     with H not a multiple of 256): LDS-tiled fp64 vector GEMM, K-split.
 //   select_kernel: one workgroup per token quantises the token's x (Q8_0), sums
 //     the K-split partials in a fixed order (deterministic) and performs the
 //     group-limited top-k as rank computations over LDS.
@@ -156,6 +157,94 @@ __global__ __launch_bounds__(256) void logits_kernel(const float *__restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ logits, T > 16
+// fp64 matrix cores (v_mfma_f64_16x16x4f64): a workgroup owns 64 tokens x 64
+// experts of one K split, a wavefront 32 x 32 as 2 x 2 MFMA tiles. x and W stay
+// fp32 in LDS (staged 32 K at a time, double-buffered) and are widened to fp64
+// as operands, so every product is exact and only the fp64 summation order
+// differs from any other evaluation. Lane l, result r of a 16 x 16 tile holds
+// row (token) l / 16 + 4 r and column (expert) l % 16.
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int LM_T = 64, LM_E = 64, LM_KB = 32;
+
+__global__ __launch_bounds__(256) void logits_mfma_kernel(const float *__restrict__ x, const float *__restrict__ W,
+                                                          int T, int E, int H, int kc, double *__restrict__ part) {
+  __shared__ float xs[2][LM_T][LM_KB + 1];
+  __shared__ float ws[2][LM_E][LM_KB + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int t0 = blockIdx.y * LM_T, e0 = blockIdx.x * LM_E, ks = blockIdx.z;
+  const int k0 = ks * kc, nst = kc / LM_KB;
+
+  // staging: 2 float4 of x and 2 of W per thread and stage
+  float4 rx[2], rw[2];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int q = tid + 256 * j, row = q >> 3, c4 = q & 7;
+      const int t = t0 + row, e = e0 + row;
+      const int64_t k = k0 + (int64_t)st * LM_KB + 4 * c4;
+      rx[j] = (t < T) ? *reinterpret_cast<const float4 *>(x + (int64_t)t * H + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rw[j] = (e < E) ? *reinterpret_cast<const float4 *>(W + (int64_t)e * H + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int q = tid + 256 * j, row = q >> 3, c = 4 * (q & 7);
+      xs[buf][row][c] = rx[j].x;
+      xs[buf][row][c + 1] = rx[j].y;
+      xs[buf][row][c + 2] = rx[j].z;
+      xs[buf][row][c + 3] = rx[j].w;
+      ws[buf][row][c] = rw[j].x;
+      ws[buf][row][c + 1] = rw[j].y;
+      ws[buf][row][c + 2] = rw[j].z;
+      ws[buf][row][c + 3] = rw[j].w;
+    }
+  };
+
+  v4d acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++) acc[a][b] = (v4d){0.0, 0.0, 0.0, 0.0};
+
+  const int ri = lane & 15, rk = lane >> 4;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < nst; st++) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) gload(st + 1);
+#pragma unroll
+    for (int kk = 0; kk < LM_KB; kk += 4) {
+      double av[2], bv[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; s2++) {
+        av[s2] = (double)xs[buf][wm * 32 + s2 * 16 + ri][kk + rk];
+        bv[s2] = (double)ws[buf][wn * 32 + s2 * 16 + ri][kk + rk];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int t = t0 + wm * 32 + a * 16 + rk + 4 * r;
+        const int e = e0 + wn * 32 + b * 16 + ri;
+        if (t < T && e < E) part[((int64_t)ks * T + t) * E + e] = acc[a][b][r];
+      }
+}
+
 // ------------------------------------------------------------------ selection
 struct SelectArgs {
   const double *part;
@@ -284,9 +373,13 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
 // ------------------------------------------------------------------ host side
 int32_t route_ksplit(const coli_moe_cfg &c, int32_t T) {
   if (T <= LD_TT && c.hidden % 256 == 0) return (c.hidden % 512 == 0) ? c.hidden / 512 : c.hidden / 256;
+  // larger T: enough K splits for about 512 workgroups of 64 x 64 (tokens x experts)
   const int nkb = c.hidden / 32;
-  for (int d = 2; d >= 1; d--)
-    if (nkb % d == 0) return d;
+  const int64_t tiles = (int64_t)((c.n_experts + LM_E - 1) / LM_E) * ((T + LM_T - 1) / LM_T);
+  const int64_t want = (512 + tiles - 1) / tiles;
+  const int cand[6] = {8, 6, 4, 3, 2, 1};
+  for (int i = 0; i < 6; i++)
+    if (cand[i] <= want && nkb % cand[i] == 0) return cand[i];
   return 1;
 }
 
@@ -304,8 +397,8 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
     dim3 grid((E + 15) / 16, 1, ks);
     hipLaunchKernelGGL((logits_kernel<16, 16, 1, 1>), grid, dim3(256), 0, s, r.x, r.W, T, E, H, H / ks, r.logits);
   } else {
-    dim3 grid((E + 63) / 64, (T + 63) / 64, ks);
-    hipLaunchKernelGGL((logits_kernel<64, 64, 4, 4>), grid, dim3(256), 0, s, r.x, r.W, T, E, H, H / ks, r.logits);
+    dim3 grid((E + LM_E - 1) / LM_E, (T + LM_T - 1) / LM_T, ks);
+    hipLaunchKernelGGL(logits_mfma_kernel, grid, dim3(256), 0, s, r.x, r.W, T, E, H, H / ks, r.logits);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
