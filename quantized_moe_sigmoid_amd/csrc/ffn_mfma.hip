@@ -14,9 +14,12 @@
 // layouts cheap to feed: lanes 0-31 take the first 16 values of a block, lanes
 // 32-63 the last 16, i.e. the low resp. high nibbles of an int4 block.
 //
-// Work: a workgroup (4 wavefronts, 2 x 2) owns 64 weight rows x 64 tokens of one
-// expert; a wavefront 32 rows x 32 tokens (gate and up together in the gate/up
-// pass). Token tiles of the union are listed by plan_kernel; the 1-D grid is
+// Work: a workgroup (4 wavefronts) owns 64 weight rows x 32 tokens of one expert;
+// wavefront (wm, wk) computes rows 32 wm .. 32 wm + 31 for all 32 tokens over the
+// blocks kb = wk mod 2 of every K stage (gate and up together in the gate/up
+// pass); the two K halves are added through LDS at the end. 32-token tiles keep
+// the padding of each expert's last tile small (the union's token counts are
+// uneven). Token tiles of the union are listed by plan_kernel; the 1-D grid is
 // remapped so that the token tiles of one (expert, row tile) land on one XCD in
 // consecutive order and share its L2 copy of the weight rows.
 #include "coli_internal.h"
@@ -27,7 +30,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int MF_ROWS = 64;  // weight rows per workgroup
-constexpr int MF_TOK = 64;   // tokens per workgroup (one token tile)
+constexpr int MF_TOK = 32;   // tokens per workgroup (one token tile)
 constexpr int MF_KC = 4;     // Q8_0 blocks per K stage staged through LDS
 
 // ------------------------------------------------------------------ plan
@@ -86,15 +89,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(FfnArgs a, int4 *__restrict_
 }
 
 // ------------------------------------------------------------------ staging
-// Per-byte sign extension of b-bit two's complement fields already isolated in
-// each byte: flip the sign bit to offset binary, add 0x80 - 2^(b-1), flip bit 7.
-// No byte carries into the next (every byte stays <= 0x80 + 2^(b-1) - 1).
-template <int BITS>
-__device__ __forceinline__ uint32_t sext_bytes(uint32_t t) {
-  constexpr uint32_t SGN = (BITS == 4) ? 0x08080808u : 0x02020202u;
-  constexpr uint32_t ADD = (BITS == 4) ? 0x78787878u : 0x7E7E7E7Eu;
-  return ((t ^ SGN) + ADD) ^ 0x80808080u;
-}
+// Packed weights enter the MFMA as int8 with the field in the top bits of its
+// byte: an int4 field w becomes the byte 16 w, an int2 field 64 w (two's
+// complement keeps the sign). One AND (and a shift) per four values, and the block
+// dots come out as exact multiples SCALE * I_b; the accumulated sums are divided
+// by SCALE at the end, exactly (a power of two).
+template <int WB>
+struct Top {
+  static constexpr int scale = (WB == 4) ? 16 : (WB == 2) ? 64 : 1;
+};
 
 // LDS tiles of one K stage of KC blocks, int8 in natural K order; rows padded by
 // 16 bytes against bank conflicts.
@@ -103,7 +106,7 @@ struct MfLds {
   static constexpr int ROWB = KC * QK + 16;  // bytes per row (and per token)
   int8_t a[2][NMAT][MF_ROWS][ROWB];
   int8_t b[2][MF_TOK][ROWB];
-  float d[2][MF_TOK][KC];
+  float d[2][MF_TOK][KC];  // block scale of each token
 };
 
 enum { MF_GATEUP = 0, MF_DOWN = 1 };
@@ -116,7 +119,7 @@ struct MfRegs {
   static constexpr int APIECES = KC * QK * WB / 8 / 16;
   static constexpr int ATOTAL = NMAT * MF_ROWS * APIECES;
   static constexpr int ALOADS = (ATOTAL + 255) / 256;  // per thread (the last may be partial)
-  static constexpr int BLOADS = MF_TOK * KC * QK / 16 / 256;
+  static constexpr int BLOADS = (MF_TOK * KC * QK / 16 + 255) / 256;
   uint4 a[ALOADS];
   uint4 b[BLOADS];
   float d;
@@ -133,8 +136,9 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   constexpr int APIECES = Regs::APIECES;
   constexpr int ATOTAL = Regs::ATOTAL;
   static_assert(ATOTAL % 64 == 0, "weight pieces: whole wavefronts");
-  static_assert(Regs::BLOADS >= 1 && MF_TOK * KC * 2 % 256 == 0, "token pieces per thread");
-  static_assert(MF_TOK * KC == 256, "one block scale per thread and stage");
+  static_assert(MF_TOK * KC * 2 == 256, "one 16-byte token piece per thread and stage");
+  static_assert(MF_TOK * KC <= 256, "at most one block scale per thread and stage");
+  static_assert(KC % 2 == 0, "the two K halves take alternate blocks");
   __shared__ Lds L;
   __shared__ int act_rows[MF_TOK];
 
@@ -148,8 +152,9 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   if (g >= *ntiles) return;
   const int4 ti = tiles[g];  // expert, first perm index (-1: shared), tokens, tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wv & 1, wk = wv >> 1;
   const int grp = lane >> 5, li = lane & 31;
   const int K = (MODE == MF_GATEUP) ? a.H : a.F;
   const int nkb = K / QK;
@@ -184,7 +189,8 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
     const int q = tid + 256 * j;
     boff[j] = (int64_t)act_rows[q / (2 * KC)] * K + (q % (2 * KC)) * 16;
   }
-  const int64_t doff = (int64_t)act_rows[tid / KC] * nkb + tid % KC;
+  const bool dthread = tid < MF_TOK * KC;
+  const int64_t doff = (int64_t)act_rows[dthread ? tid / KC : 0] * nkb + tid % KC;
 
   auto gload = [&](int s, Regs &r) {
     const int kb0 = s * KC;  // first block of the stage
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
 #pragma unroll
     for (int j = 0; j < Regs::BLOADS; j++)
       r.b[j] = *reinterpret_cast<const uint4 *>(asrc + boff[j] + (int64_t)kb0 * QK);
-    r.d = __int_as_float(dsrc[doff + kb0].x);
+    if (dthread) r.d = __int_as_float(dsrc[doff + kb0].x);
   };
 
   auto lstore = [&](int buf, const Regs &r) {
@@ -215,14 +221,14 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       } else if constexpr (WB == 4) {
         // one 16-byte block: values 0..15 in the low nibbles, 16..31 in the high ones
         uint4 lo, hi;
-        lo.x = sext_bytes<4>(v.x & 0x0F0F0F0Fu);
-        lo.y = sext_bytes<4>(v.y & 0x0F0F0F0Fu);
-        lo.z = sext_bytes<4>(v.z & 0x0F0F0F0Fu);
-        lo.w = sext_bytes<4>(v.w & 0x0F0F0F0Fu);
-        hi.x = sext_bytes<4>((v.x >> 4) & 0x0F0F0F0Fu);
-        hi.y = sext_bytes<4>((v.y >> 4) & 0x0F0F0F0Fu);
-        hi.z = sext_bytes<4>((v.z >> 4) & 0x0F0F0F0Fu);
-        hi.w = sext_bytes<4>((v.w >> 4) & 0x0F0F0F0Fu);
+        lo.x = (v.x << 4) & 0xF0F0F0F0u;
+        lo.y = (v.y << 4) & 0xF0F0F0F0u;
+        lo.z = (v.z << 4) & 0xF0F0F0F0u;
+        lo.w = (v.w << 4) & 0xF0F0F0F0u;
+        hi.x = v.x & 0xF0F0F0F0u;
+        hi.y = v.y & 0xF0F0F0F0u;
+        hi.z = v.z & 0xF0F0F0F0u;
+        hi.w = v.w & 0xF0F0F0F0u;
         *reinterpret_cast<uint4 *>(dst + pc * 32) = lo;
         *reinterpret_cast<uint4 *>(dst + pc * 32 + 16) = hi;
       } else {
@@ -231,14 +237,14 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
         for (int h = 0; h < 2; h++) {
           const uint32_t w0 = h ? v.z : v.x, w1 = h ? v.w : v.y;
           uint4 o0, o1;
-          o0.x = sext_bytes<2>(w0 & 0x03030303u);
-          o0.y = sext_bytes<2>(w1 & 0x03030303u);
-          o0.z = sext_bytes<2>((w0 >> 2) & 0x03030303u);
-          o0.w = sext_bytes<2>((w1 >> 2) & 0x03030303u);
-          o1.x = sext_bytes<2>((w0 >> 4) & 0x03030303u);
-          o1.y = sext_bytes<2>((w1 >> 4) & 0x03030303u);
-          o1.z = sext_bytes<2>((w0 >> 6) & 0x03030303u);
-          o1.w = sext_bytes<2>((w1 >> 6) & 0x03030303u);
+          o0.x = (w0 << 6) & 0xC0C0C0C0u;
+          o0.y = (w1 << 6) & 0xC0C0C0C0u;
+          o0.z = (w0 << 4) & 0xC0C0C0C0u;
+          o0.w = (w1 << 4) & 0xC0C0C0C0u;
+          o1.x = (w0 << 2) & 0xC0C0C0C0u;
+          o1.y = (w1 << 2) & 0xC0C0C0C0u;
+          o1.z = w0 & 0xC0C0C0C0u;
+          o1.w = w1 & 0xC0C0C0C0u;
           *reinterpret_cast<uint4 *>(dst + pc * 64 + h * 32) = o0;
           *reinterpret_cast<uint4 *>(dst + pc * 64 + h * 32 + 16) = o1;
         }
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       const int q = tid + 256 * j;
       *reinterpret_cast<uint4 *>(&L.b[buf][q / (2 * KC)][(q % (2 * KC)) * 16]) = r.b[j];
     }
-    L.d[buf][tid / KC][tid % KC] = r.d;
+    if (dthread) L.d[buf][tid / KC][tid % KC] = r.d;
   };
 
   float acc[NMAT][16];
@@ -261,11 +267,10 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   // one stage from LDS: per block, an exact int32 block dot by MFMA, then the scale
   auto compute = [&](int buf) {
     const int8_t *arow0 = &L.a[buf][0][wm * 32 + li][16 * grp];
-    const int8_t *brow = &L.b[buf][wn * 32 + li][16 * grp];
-#pragma unroll
-    for (int kb = 0; kb < KC; kb++) {
+    const int8_t *brow = &L.b[buf][li][16 * grp];
+    for (int kb = wk; kb < KC; kb += 2) {
       const v4i bv = *reinterpret_cast<const v4i *>(brow + kb * QK);
-      const float d = L.d[buf][wn * 32 + li][kb];
+      const float d = L.d[buf][li][kb];
 #pragma unroll
       for (int m = 0; m < NMAT; m++) {
         const v4i av = *reinterpret_cast<const v4i *>(arow0 + m * (MF_ROWS * ROWB) + kb * QK);
@@ -277,6 +282,8 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
     }
   };
 
+  // stage s: the next stage's global loads go out before this stage's compute and
+  // land in the other LDS buffer afterwards (one barrier per stage)
   const int ns = nkb / KC;
   {
     Regs r;
@@ -292,10 +299,33 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
     if (more) lstore((s + 1) & 1, r);
     __syncthreads();
   }
+  if constexpr (Top<WB>::scale != 1) {
+    constexpr float inv = 1.0f / Top<WB>::scale;
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[m][r] *= inv;
+  }
+
+  // add the K half of wavefronts wk = 1 to that of wk = 0 (the stage buffers are free)
+  float *red = reinterpret_cast<float *>(&L.a[0][0][0][0]);
+  static_assert(sizeof(L.a) >= 2 * 64 * NMAT * 16 * sizeof(float), "reduction buffer");
+  if (wk == 1) {
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) red[((wm * NMAT + m) * 16 + r) * 64 + lane] = acc[m][r];
+  }
+  __syncthreads();
+  if (wk == 1) return;
+#pragma unroll
+  for (int m = 0; m < NMAT; m++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[m][r] += red[((wm * NMAT + m) * 16 + r) * 64 + lane];
 
   // epilogue. Result r of this lane: row r0 + 32 wm + 8 (r / 4) + 4 grp + r % 4,
-  // token wn * 32 + li of the tile.
-  const int i = ti.w * MF_TOK + wn * 32 + li;
+  // token li of the tile.
+  const int i = ti.w * MF_TOK + li;
   const bool valid = i < ti.z;
   int out_row = 0;
   if (valid) out_row = (ti.y < 0) ? P + i : a.perm[ti.y + i];
