@@ -665,6 +665,150 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident GEMV: the shapes whose row is one chunk per lane (CPL = 1) and
+// whose tile fits in registers. Every lane loads all of its tile's weight chunks
+// once, right after the slot is known, and keeps them across the token passes, so
+// the weights of an expert are read from memory exactly once whatever its token
+// count. Activations (Q8_0 rows, L2-resident) are read per pass straight into
+// registers, without LDS staging. Same arithmetic and summation tree as
+// gemv_fast_kernel.
+template <int WB, int LPR, int MODE, int WR, int NTC>
+__global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
+  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int RPI = WAVE / LPR;
+  constexpr int R = WR / RPI;  // rows per lane
+  constexpr int CW = Fmt<WB>::CHUNK / 4;
+  constexpr int BPC = Fmt<WB>::BPC;
+  constexpr int TILE = 4 * WR;
+  constexpr int V = R * NMAT * NTC;
+  constexpr int SCAT = cmin<ilog2(V), ilog2(LPR)>::v;
+  constexpr int KEPT = V >> SCAT;
+  constexpr int WMASK = (LPR >> SCAT) - 1;
+  static_assert(R * RPI == WR && R * NMAT * CW <= 64, "tile weights fit in 64 registers per lane");
+  static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
+  static_assert(NTC * TILE <= 256, "one epilogue value per thread and pass");
+
+  __shared__ SlotLds SL;
+  __shared__ float obuf[NMAT][NTC][TILE];
+  int e, n, beg;
+  bool shared;
+  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rs = lane / LPR, sub = lane % LPR;
+  const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
+  const int nkb = K / QK;
+  const int64_t rb = row_bytes(WB, K);
+  const int64_t rbh = row_bytes(WB, a.H);
+  const uint8_t *blob = a.experts + (int64_t)e * a.blob_bytes;
+  const uint8_t *mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+  const uint8_t *mat1 = blob + (int64_t)a.F * rbh;
+  const int r0 = blockIdx.x * TILE;
+
+  uint32_t w[R][NMAT][CW];
+#pragma unroll
+  for (int j = 0; j < R; j++) {
+    const int64_t roff = (int64_t)(r0 + wv * WR + j * RPI + rs) * rb + (int64_t)sub * Fmt<WB>::CHUNK;
+#pragma unroll
+    for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff, w[j][m]);
+  }
+  // epilogue value of this thread: token pt, row r0 + pi of the tile
+  const int pt = tid / TILE, pi = tid % TILE;
+  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  float s0 = 0.0f, s1 = 0.0f;
+  if (pt < NTC) {
+    if constexpr (MODE == MODE_GATEUP) {
+      s0 = sc[r0 + pi];
+      s1 = sc[a.F + r0 + pi];
+    } else {
+      s0 = sc[2 * a.F + r0 + pi];
+    }
+  }
+  const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
+  const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+
+  for (int tc = 0; tc < n; tc += NTC) {
+    const int nt = min(NTC, n - tc);
+    int orow[NTC];
+    Act<WB> act[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; t++) {
+      const int i = tc + min(t, nt - 1);  // past nt: repeat the last token, write nothing
+      const int p = slot_pair(a, SL, shared, beg, i);
+      orow[t] = p;
+      const int64_t arow = (MODE == MODE_GATEUP) ? (shared ? i : p / a.k) : p;
+      load_act<WB>(asrc + arow * K + sub * BPC * QK, dsrc + arow * nkb + sub * BPC, act[t]);
+    }
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < R; j++)
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) {
+        // unpack per pass: kept out of the pass loop the unpacked tile would need
+        // twice the registers (the empty asm makes the packed words opaque)
+#pragma unroll
+        for (int q = 0; q < CW; q++) asm volatile("" : "+v"(w[j][m][q]));
+        int u[Unp<WB>::N];
+        unpack_chunk<WB>(w[j][m], u);
+#pragma unroll
+        for (int t = 0; t < NTC; t++) acc[(j * NMAT + m) * NTC + t] += dot_unpacked<WB>(u, act[t]);
+      }
+    int base = 0;
+    reduce_scatter<V, LPR / 2>(acc, lane, base);
+    if ((lane & WMASK) == 0) {
+#pragma unroll
+      for (int i = 0; i < KEPT; i++) {
+        const int o = base + i;
+        const int t = o % NTC, m = (o / NTC) % NMAT, j = o / (NTC * NMAT);
+        obuf[m][t][wv * WR + j * RPI + rs] = acc[i];
+      }
+    }
+    __syncthreads();
+    if (pt < NTC) {
+      const int r = r0 + pi;
+      const bool live = pt < nt;
+      int out = orow[0];
+#pragma unroll
+      for (int t = 1; t < NTC; t++)
+        if (pt == t) out = orow[t];
+      if constexpr (MODE == MODE_GATEUP) {
+        // a Q8_0 block of h = 32 consecutive rows = 32 consecutive threads of one token
+        const float g = s0 * obuf[0][pt][pi];
+        const float u = s1 * obuf[NMAT - 1][pt][pi];
+        const float v = (g / (1.0f + expf(-g))) * u;
+        float am = fabsf(v);
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        const float d = am / 127.0f;
+        int q = 0;
+        if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
+        int sum = q;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+        if (live) {
+          a.hq[(int64_t)out * a.F + r] = (int8_t)q;
+          if ((pi & 31) == 0) a.hds[(int64_t)out * (a.F / QK) + r / QK] = make_int2(__float_as_int(d), sum);
+        }
+      } else {
+        if (live) a.ypair[(int64_t)out * a.H + r] = s0 * obuf[0][pt][pi];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int WB, int LPR, int MODE>
+static hipError_t launch_reg(const FfnArgs &a, int nrows, int slots, hipStream_t s) {
+  constexpr int WR = (MODE == MODE_DOWN && LPR < 64) ? 16 : 8;
+  constexpr int TILE = 4 * WR;
+  if (nrows % TILE) return hipErrorNotSupported;
+  hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), dim3(nrows / TILE, slots), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // lanes per row: largest power of two <= 64 dividing the chunks per row
 static int pick_lpr(int nchunk) {
   int l = 64;
@@ -698,6 +842,14 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   const int lpr = pick_lpr(nchunk);
   const int cpl = nchunk / lpr;
   const int slots = a.has_shared + min(a.E, a.T * a.k);
+  // one chunk per lane and row, and the tile fits in registers: weights stay resident
+  constexpr int NMATC = (MODE == MODE_GATEUP) ? 2 : 1;
+  if constexpr (WB != 2 && (Fmt<WB>::CHUNK / 4) * NMATC * 8 <= 64) {
+    if (cpl == 1 && (lpr == 64 || lpr == 32)) {
+      hipError_t r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
+      if (r != hipErrorNotSupported) return r;
+    }
+  }
   // the batched kernel for the shapes it is instantiated for
   if (lpr == 64 || lpr == 32) {
     hipError_t r = hipErrorNotSupported;
