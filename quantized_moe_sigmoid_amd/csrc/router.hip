@@ -264,23 +264,39 @@ constexpr int SEL_NT = 256;  // threads per token
 // (v, i) ranks before (v2, i2): larger value first, then lower index
 __device__ __forceinline__ bool before(double v2, int i2, double v, int i) { return v2 > v || (v2 == v && i2 < i); }
 
-// One workgroup per token. Every step is a rank computation over LDS, so the
-// selection costs a few passes over E values instead of k dependent arg-max
-// reductions:
-//   c_e in LDS; the rank of e inside its group (among c, lower index first) puts
-//   the two best values of each group in place; the group score is their sum;
-//   the rank of a group among the group scores decides whether it is kept;
-//   experts of dropped groups get c = -inf; the rank of e among all c is its
-//   output slot when below k. Ranks are exact (no ties: the index breaks them).
+// number of entries j in [lo, lo + cnt) of (val[j], id(j)) that rank before (v, i); the
+// LDS reads are unrolled so that several are in flight
+template <typename IdOf>
+__device__ __forceinline__ int count_before(const double *val, int lo, int cnt, double v, int i, IdOf id) {
+  int r = 0;
+#pragma unroll 8
+  for (int j = lo; j < lo + cnt; j++) r += before(val[j], id(j), v, i) ? 1 : 0;
+  return r;
+}
+
+// One workgroup per token. Every step is a rank computation over LDS:
+//   c_e in LDS; the rank of e inside its group (c desc, lower index first) gives
+//   the two best values of each group, whose sum is the group score; the rank of a
+//   group among the group scores decides whether it is kept. An expert with k or
+//   more better experts in its own group cannot be among the k best, so only the
+//   experts of kept groups with in-group rank below k are candidates; the rank of
+//   a candidate among the candidates is its rank among all kept experts (every
+//   expert ranked before a selected one is a candidate), hence its output slot
+//   when below k. With one group the in-group rank already is the slot. Ranks are
+//   exact (the index breaks every tie).
 // The token's row of x is quantised (Q8_0) first, by the whole workgroup.
 template <int EPT>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   __shared__ double cs[SEL_NT * EPT];
+  __shared__ double cand_c[SEL_NT * EPT];
+  __shared__ int cand_e[SEL_NT * EPT];
+  __shared__ double cand_s[SEL_NT * EPT];
   __shared__ double gtop[64][2];
   __shared__ double gsc[64];
   __shared__ int gkeep[64];
   __shared__ int sel_e[64];
   __shared__ double sel_s[64];
+  __shared__ int ncand;
   const int t = blockIdx.x, tid = threadIdx.x;
   const int E = a.E, G = a.G, k = a.k, m = E / G;
 
@@ -317,46 +333,55 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
     }
   }
   if (tid < 64) sel_e[tid] = -1;
+  if (tid == 0) ncand = 0;
   __syncthreads();
 
-  // the two best c of each group
+  // rank of each expert inside its group
+  int rin[EPT];
+  auto self = [](int j) { return j; };
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
     const int e = tid + SEL_NT * i;
+    rin[i] = 0x7fffffff;
     if (e < E) {
-      const int lo = (e / m) * m;
-      int r = 0;
-      for (int e2 = lo; e2 < lo + m; e2++) r += before(cs[e2], e2, c[i], e) ? 1 : 0;
-      if (r < 2) gtop[e / m][r] = c[i];
+      rin[i] = count_before(cs, (e / m) * m, m, c[i], e, self);
+      if (G > 1 && rin[i] < 2) gtop[e / m][rin[i]] = c[i];
     }
   }
-  __syncthreads();
-  if (tid < G) gsc[tid] = (m > 1) ? gtop[tid][0] + gtop[tid][1] : gtop[tid][0];
-  __syncthreads();
-  if (tid < G) {
-    int r = 0;
-    for (int g2 = 0; g2 < G; g2++) r += before(gsc[g2], g2, gsc[tid], tid) ? 1 : 0;
-    gkeep[tid] = r < a.Gk;
-  }
-  __syncthreads();
+  if (G == 1) {
 #pragma unroll
-  for (int i = 0; i < EPT; i++) {
-    const int e = tid + SEL_NT * i;
-    if (e < E && !gkeep[e / m]) {
-      c[i] = -INFINITY;
-      cs[e] = -INFINITY;
+    for (int i = 0; i < EPT; i++) {
+      const int e = tid + SEL_NT * i;
+      if (e < E && rin[i] < k) {
+        sel_e[rin[i]] = e;
+        sel_s[rin[i]] = s[i];
+      }
     }
-  }
-  __syncthreads();
+  } else {
+    __syncthreads();
+    if (tid < G) gsc[tid] = (m > 1) ? gtop[tid][0] + gtop[tid][1] : gtop[tid][0];
+    __syncthreads();
+    if (tid < G) gkeep[tid] = count_before(gsc, 0, G, gsc[tid], tid, self) < a.Gk;
+    __syncthreads();
+    // candidates: kept groups, in-group rank below k (slot order is free: ranks decide)
 #pragma unroll
-  for (int i = 0; i < EPT; i++) {
-    const int e = tid + SEL_NT * i;
-    if (e < E && c[i] != -INFINITY) {
-      int r = 0;
-      for (int e2 = 0; e2 < E; e2++) r += before(cs[e2], e2, c[i], e) ? 1 : 0;
+    for (int i = 0; i < EPT; i++) {
+      const int e = tid + SEL_NT * i;
+      if (e < E && rin[i] < k && gkeep[e / m]) {
+        const int q = atomicAdd(&ncand, 1);
+        cand_c[q] = c[i];
+        cand_s[q] = s[i];
+        cand_e[q] = e;
+      }
+    }
+    __syncthreads();
+    const int nc = ncand;
+    for (int q = tid; q < nc; q += SEL_NT) {
+      const int e = cand_e[q];
+      const int r = count_before(cand_c, 0, nc, cand_c[q], e, [&](int j) { return cand_e[j]; });
       if (r < k) {
         sel_e[r] = e;
-        sel_s[r] = s[i];
+        sel_s[r] = cand_s[q];
       }
     }
   }
