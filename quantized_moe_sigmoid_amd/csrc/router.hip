@@ -325,8 +325,18 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
     s[i] = 0.0;
     c[i] = -INFINITY;
     if (e < E) {
+      // K-split partials summed in split order; loads issued eight at a time
       double z = 0.0;
-      for (int ks = 0; ks < a.ksplit; ks++) z += a.part[((int64_t)ks * a.T + t) * E + e];
+      const double *pp = a.part + (int64_t)t * E + e;
+      const int64_t stride = (int64_t)a.T * E;
+      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = (k0 + j < a.ksplit) ? pp[(k0 + j) * stride] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (k0 + j < a.ksplit) z += v[j];
+      }
       s[i] = 1.0 / (1.0 + exp(-z));
       c[i] = s[i] + (double)a.bias[e];
       cs[e] = c[i];
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------------ host side
 int32_t route_ksplit(const coli_moe_cfg &c, int32_t T) {
-  if (T <= LD_TT && c.hidden % 256 == 0) return (c.hidden % 512 == 0) ? c.hidden / 512 : c.hidden / 256;
+  if (T <= LD_TT && c.hidden % 256 == 0) return c.hidden / 256;  // 256-wide K chunks: enough workgroups at decode sizes
   // larger T: enough K splits for about 512 workgroups of 64 x 64 (tokens x experts)
   const int nkb = c.hidden / 32;
   const int64_t tiles = (int64_t)((c.n_experts + LM_E - 1) / LM_E) * ((T + LM_T - 1) / LM_T);
