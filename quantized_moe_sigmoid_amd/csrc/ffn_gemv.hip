@@ -802,7 +802,10 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
 
 template <int WB, int LPR, int MODE>
 static hipError_t launch_reg(const FfnArgs &a, int nrows, int slots, hipStream_t s) {
-  constexpr int WR = (MODE == MODE_DOWN && LPR < 64) ? 16 : 8;
+  // rows per wavefront: gate/up 8 (two matrices, 32-row tiles = one Q8_0 block of h),
+  // down 16 (64-row tiles; measured best for both 32 and 64 lanes per row)
+  constexpr int WRMAX = 64 * (WAVE / LPR) / (Fmt<WB>::CHUNK / 4);  // 64 registers of weights
+  constexpr int WR = (MODE == MODE_DOWN) ? (WRMAX < 16 ? WRMAX : 16) : 8;
   constexpr int TILE = 4 * WR;
   if (nrows % TILE) return hipErrorNotSupported;
   hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), dim3(nrows / TILE, slots), dim3(256), 0, s, a);
