@@ -673,7 +673,10 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
 // count. Activations (Q8_0 rows, L2-resident) are read per pass straight into
 // registers, without LDS staging. Same arithmetic and summation tree as
 // gemv_fast_kernel.
-template <int WB, int LPR, int MODE, int WR, int NTC>
+// DIRECT (batches that hit most experts, route given): grid row y is expert y - S
+// itself, so the tile's weight loads go out together with the load of the route
+// instead of after the slot is resolved; an expert without tokens exits.
+template <int WB, int LPR, int MODE, int WR, int NTC, bool DIRECT>
 __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int RPI = WAVE / LPR;
@@ -691,9 +694,25 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
 
   __shared__ SlotLds SL;
   __shared__ float obuf[NMAT][NTC][TILE];
-  int e, n, beg;
+  int e, n = 0, beg = 0;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+  constexpr int QD = LOCAL_GROUP_MAX_P / 64;
+  int ev[QD];
+  if constexpr (DIRECT) {
+    shared = a.has_shared && blockIdx.y == 0;
+    e = shared ? a.E : (int)blockIdx.y - a.has_shared;
+    if (!shared && threadIdx.x < 64) {  // the route, issued before the weights
+      const int P = a.T * a.k;
+#pragma unroll
+      for (int i = 0; i < QD; i++) {
+        const int p = (int)threadIdx.x + 64 * i;
+        ev[i] = -1;
+        if (p < P) ev[i] = a.idx[p];
+      }
+    }
+  } else {
+    if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rs = lane / LPR, sub = lane % LPR;
@@ -712,6 +731,27 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
     const int64_t roff = (int64_t)(r0 + wv * WR + j * RPI + rs) * rb + (int64_t)sub * Fmt<WB>::CHUNK;
 #pragma unroll
     for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff, w[j][m]);
+  }
+  if constexpr (DIRECT) {  // this expert's pairs, ascending, while the weights are in flight
+    if (shared) {
+      n = a.T;
+    } else {
+      if (tid < 64) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < QD; i++) {
+          const bool m = ev[i] == e;
+          const uint64_t b = __ballot(m);
+          if (m) SL.pairs[cnt + __popcll(b & below)] = lane + 64 * i;
+          cnt += __popcll(b);
+        }
+        if (lane == 0) SL.n = cnt;
+      }
+      __syncthreads();
+      n = SL.n;
+    }
+    if (n == 0) return;
   }
   // epilogue value of this thread: token pt, row r0 + pi of the tile
   const int pt = tid / TILE, pi = tid % TILE;
@@ -811,11 +851,22 @@ static hipError_t launch_reg(const FfnArgs &a, int nrows, int slots, hipStream_t
   // token passes: two tokens when the experts average two or more (gate/up), else one
   // (fewer accumulators, one more wave per SIMD; measured faster for down and for
   // small batches)
-  const bool two = MODE == MODE_GATEUP && (int64_t)a.T * a.k >= 2 * (int64_t)a.E;
-  if (two)
-    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), dim3(nrows / TILE, slots), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1>), dim3(nrows / TILE, slots), dim3(256), 0, s, a);
+  const bool dense = (int64_t)a.T * a.k >= 2 * (int64_t)a.E;  // most experts hit (about 86% or more)
+  const bool two = MODE == MODE_GATEUP && dense;
+  // grid by expert when the route is at hand and most experts are hit
+  const bool direct = dense && a.idx != nullptr;
+  const dim3 grid(nrows / TILE, direct ? a.E + a.has_shared : slots);
+  if (direct) {
+    if (two)
+      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (two)
+      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
