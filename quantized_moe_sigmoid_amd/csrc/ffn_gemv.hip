@@ -673,6 +673,15 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
 // count. Activations (Q8_0 rows, L2-resident) are read per pass straight into
 // registers, without LDS staging. Same arithmetic and summation tree as
 // gemv_fast_kernel.
+// Barrier for LDS hand-offs only: wait for this wavefront's LDS accesses
+// (lgkmcnt = 0), then s_barrier. __syncthreads() also waits for every outstanding
+// global load and store (vmcnt = 0), i.e. for the epilogue's stores to reach
+// memory, which under full HBM load costs microseconds per pass.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0 (gfx9 encoding)
+  __builtin_amdgcn_s_barrier();
+}
+
 // DIRECT (batches that hit most experts, route given): grid row y is expert y - S
 // itself, so the tile's weight loads go out together with the load of the route
 // instead of after the slot is resolved; an expert without tokens exits.
@@ -748,7 +757,7 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
         }
         if (lane == 0) SL.n = cnt;
       }
-      __syncthreads();
+      lds_barrier();
       n = SL.n;
     }
     if (n == 0) return;
@@ -806,7 +815,7 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
         obuf[m][t][wv * WR + j * RPI + rs] = acc[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (pt < NTC) {
       const int r = r0 + pi;
       const bool live = pt < nt;
@@ -836,7 +845,7 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
         if (live) a.ypair[(int64_t)out * a.H + r] = s0 * obuf[0][pt][pi];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
