@@ -20,7 +20,7 @@ __host__ __device__ inline int64_t row_bytes(int wfmt, int n) { return (int64_t)
 
 struct WsLayout {
   // byte offsets into the workspace (all 256-byte aligned)
-  size_t xq, xds, hq, hds, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, total;
+  size_t xq, xd, hq, hd, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, total;
 };
 
 // Workspace layout for T tokens (valid cfg assumed).
@@ -36,7 +36,7 @@ struct GroupOut {
 constexpr int LOCAL_GROUP_MAX_P = 512;  // pairs a GEMV workgroup groups by itself (decode-sized batches)
 
 // ---- launchers (host side, one per kernel family); return hipError_t
-hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, int2 *ds, hipStream_t s);
+hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, hipStream_t s);
 
 struct RouteLaunch {
   const coli_moe_cfg *cfg;
@@ -47,8 +47,8 @@ struct RouteLaunch {
   int32_t ksplit;
   int32_t *idx;
   float *w;
-  int8_t *xq;        // quantise x into xq/xds in the selection kernel when non-null
-  int2 *xds;
+  int8_t *xq;        // quantise x into xq/xd in the selection kernel when non-null
+  float *xd;
 };
 hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid);
 hipError_t launch_group(const coli_moe_cfg &c, const int32_t *idx, int32_t T, int32_t *cnt, int32_t *off,
@@ -63,9 +63,9 @@ struct FfnArgs {
   const int32_t *off, *perm, *active, *nact;  // grouping arrays (read when idx == nullptr)
   const int32_t *idx;  // route [T][k]: each workgroup groups locally when set (T*k <= LOCAL_GROUP_MAX_P)
   const int8_t *xq;   // [T][H]
-  const int2 *xds;    // [T][H/32] {d bits, block sum}
+  const float *xd;    // [T][H/32] Q8_0 block scales
   int8_t *hq;         // [P+T][F]
-  int2 *hds;          // [P+T][F/32]
+  float *hd;          // [P+T][F/32]
   float *ypair;       // [P+T][H]
 };
 hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s);

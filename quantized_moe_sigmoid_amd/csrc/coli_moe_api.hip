@@ -15,9 +15,9 @@ WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit) {
   WsLayout L{};
   size_t o = 0;
   L.xq = o;     o = align256(o + (size_t)T * H);
-  L.xds = o;    o = align256(o + (size_t)T * (H / QK) * sizeof(int2));
+  L.xd = o;     o = align256(o + (size_t)T * (H / QK) * sizeof(float));
   L.hq = o;     o = align256(o + R * F);
-  L.hds = o;    o = align256(o + R * (F / QK) * sizeof(int2));
+  L.hd = o;     o = align256(o + R * (F / QK) * sizeof(float));
   L.ypair = o;  o = align256(o + R * H * sizeof(float));
   L.logits = o; o = align256(o + (size_t)ksplit * T * E * sizeof(double));
   L.idx = o;    o = align256(o + P * sizeof(int32_t));
@@ -36,7 +36,7 @@ WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit) {
 static constexpr size_t GEMV_LDS_LIMIT = 64 * 1024;
 
 static size_t gemv_lds(int K) {
-  return (size_t)GEMV_NT * K + (size_t)GEMV_NT * (K / QK) * sizeof(int2) + (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) +
+  return (size_t)GEMV_NT * K + (size_t)GEMV_NT * (K / QK) * sizeof(float) + (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) +
          2 * GEMV_NT * sizeof(int);
 }
 
@@ -94,7 +94,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
                        hipStream_t s, hipEvent_t *ev, bool quantize_x) {
   int st;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
-  if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), nullptr, at<int2>(ws, L.xds), s))))
+  if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), at<float>(ws, L.xd), s))))
     return st;
   FfnArgs a{};
   a.experts = static_cast<const uint8_t *>(w.experts);
@@ -112,9 +112,9 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.nact = nact;
   a.idx = local_idx;
   a.xq = at<int8_t>(ws, L.xq);
-  a.xds = at<int2>(ws, L.xds);
+  a.xd = at<float>(ws, L.xd);
   a.hq = at<int8_t>(ws, L.hq);
-  a.hds = at<int2>(ws, L.hds);
+  a.hd = at<float>(ws, L.hd);
   a.ypair = at<float>(ws, L.ypair);
   // Batches past the decode size run the expert FFNs as grouped GEMMs on the
   // matrix cores; a tile plan of the union comes first.
@@ -168,7 +168,7 @@ static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const 
   r.idx = idx;
   r.w = tw;
   r.xq = at<int8_t>(ws, L.xq);
-  r.xds = at<int2>(ws, L.xds);
+  r.xd = at<float>(ws, L.xd);
   // decode-sized batches: every GEMV workgroup groups the route itself
   const bool local = (int64_t)T * cfg->top_k <= LOCAL_GROUP_MAX_P;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
@@ -209,7 +209,7 @@ int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q
   if (rows == 0) return COLI_OK;
   if (!x || !q || !d) return COLI_E_INVALID;
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4)) return COLI_E_ALIGN;
-  return dev(launch_q8_0(x, rows, cols, q, d, nullptr, static_cast<hipStream_t>(stream)));
+  return dev(launch_q8_0(x, rows, cols, q, d, static_cast<hipStream_t>(stream)));
 }
 
 int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,

@@ -10,10 +10,13 @@
 //   I_b = sum over block b of xq * wq         (v_dot4_i32_i8, exact int32)
 //   acc = sum_b d_b * I_b                     (fp32)
 //   out = s_row * acc
-// Packed int4 / int2 fields are two's complement; XOR with 0x88.. / 0xAA.. turns
-// them into offset-binary u = w + 8 / w + 2 (0..15 / 0..3), so a plain signed
-// dot4 applies and I_b = dot(xq, u) - 8 * sum(xq) (resp. 2 * sum), with the
-// block sum of xq precomputed next to its scale.
+// Packed int4 / int2 fields are two's complement. A shift and a mask move each
+// field into the top bits of its own byte, where the byte reads as S * w (S = 16
+// for int4, 64 for int2) with no sign fix-up, so the signed dot4 gives S * I_b
+// exactly (|S * I_b| < 2^24, so its fp32 conversion is exact too). Every fp32
+// step below then carries the factor S, a power of two that commutes with
+// rounding, and the row scale absorbs it: (s_row / S) * (S * acc) is the same
+// fp32 number as s_row * acc.
 //
 // Lane mapping: the 16-byte "chunk" of a packed row is one Q8_0 block for int4,
 // half of one for int8 (the two halves go to one lane as a 32-byte chunk) and
@@ -23,7 +26,7 @@
 // Activations of up to GEMV_NT tokens are staged in LDS once per workgroup.
 //
 // Gate/up epilogue (fused): h = silu(g) * u in fp32, then Q8_0 of the 32 rows of
-// the tile (one block of h per token): hq int8 and {hd, sum hq}.
+// the tile (one block of h per token): hq int8 and hd fp32.
 // Down epilogue: y fp32 rows, written per token as 32 consecutive floats.
 #include "coli_internal.h"
 
@@ -33,18 +36,21 @@ template <int WB>
 struct Fmt;
 template <>
 struct Fmt<4> {
-  static constexpr int CHUNK = 16;  // bytes per lane chunk
-  static constexpr int BPC = 1;     // Q8_0 blocks per chunk
+  static constexpr int CHUNK = 16;         // bytes per lane chunk
+  static constexpr int BPC = 1;            // Q8_0 blocks per chunk
+  static constexpr float INV = 0.0625f;    // 1 / S: the top-bit bytes read 16 * w
 };
 template <>
 struct Fmt<8> {
   static constexpr int CHUNK = 32;
   static constexpr int BPC = 1;
+  static constexpr float INV = 1.0f;
 };
 template <>
 struct Fmt<2> {
   static constexpr int CHUNK = 16;
   static constexpr int BPC = 2;
+  static constexpr float INV = 0.015625f;  // the top-bit bytes read 64 * w
 };
 
 __device__ __forceinline__ int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
@@ -53,52 +59,49 @@ __device__ __forceinline__ int dot4(int a, int b, int c) { return __builtin_amdg
 // the activation block scale(s); returns the fp32 contribution.
 template <int WB>
 __device__ __forceinline__ float chunk_dot(const uint32_t (&wq)[Fmt<WB>::CHUNK / 4], const int8_t *xa,
-                                           const int2 *xds);
+                                           const float *xd);
 
 template <>
-__device__ __forceinline__ float chunk_dot<4>(const uint32_t (&wq)[4], const int8_t *xa, const int2 *xds) {
+__device__ __forceinline__ float chunk_dot<4>(const uint32_t (&wq)[4], const int8_t *xa, const float *xd) {
   const int4 xl = *reinterpret_cast<const int4 *>(xa);
   const int4 xh = *reinterpret_cast<const int4 *>(xa + 16);
-  const int2 ds = xds[0];
   const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
-  int acc = -8 * ds.y;
+  int acc = 0;  // 16 * I_b
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t t = wq[i] ^ 0x88888888u;
-    acc = dot4((int)(t & 0x0F0F0F0Fu), xv[i], acc);
-    acc = dot4((int)((t >> 4) & 0x0F0F0F0Fu), xv[4 + i], acc);
+    acc = dot4((int)((wq[i] << 4) & 0xF0F0F0F0u), xv[i], acc);
+    acc = dot4((int)(wq[i] & 0xF0F0F0F0u), xv[4 + i], acc);
   }
-  return __int_as_float(ds.x) * (float)acc;
+  return xd[0] * (float)acc;
 }
 
 template <>
-__device__ __forceinline__ float chunk_dot<8>(const uint32_t (&wq)[8], const int8_t *xa, const int2 *xds) {
+__device__ __forceinline__ float chunk_dot<8>(const uint32_t (&wq)[8], const int8_t *xa, const float *xd) {
   const int4 xl = *reinterpret_cast<const int4 *>(xa);
   const int4 xh = *reinterpret_cast<const int4 *>(xa + 16);
   const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
   int acc = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) acc = dot4((int)wq[i], xv[i], acc);
-  return __int_as_float(xds[0].x) * (float)acc;
+  return xd[0] * (float)acc;
 }
 
 template <>
-__device__ __forceinline__ float chunk_dot<2>(const uint32_t (&wq)[4], const int8_t *xa, const int2 *xds) {
+__device__ __forceinline__ float chunk_dot<2>(const uint32_t (&wq)[4], const int8_t *xa, const float *xd) {
   float r = 0.0f;
 #pragma unroll
   for (int blk = 0; blk < 2; blk++) {
     const int4 xl = *reinterpret_cast<const int4 *>(xa + 32 * blk);
     const int4 xh = *reinterpret_cast<const int4 *>(xa + 32 * blk + 16);
     const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
-    const int2 ds = xds[blk];
-    int acc = -2 * ds.y;
+    int acc = 0;  // 64 * I_b
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const uint32_t t = wq[2 * blk + h] ^ 0xAAAAAAAAu;
+      const uint32_t t = wq[2 * blk + h];
 #pragma unroll
-      for (int m = 0; m < 4; m++) acc = dot4((int)((t >> (2 * m)) & 0x03030303u), xv[2 * m + h], acc);
+      for (int m = 0; m < 4; m++) acc = dot4((int)((t << (6 - 2 * m)) & 0xC0C0C0C0u), xv[2 * m + h], acc);
     }
-    r += __int_as_float(ds.x) * (float)acc;
+    r += xd[blk] * (float)acc;
   }
   return r;
 }
@@ -119,9 +122,9 @@ __device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<
   }
 }
 
-// Split form of chunk_dot for the batched kernel: the unpacked weight bytes of a
-// chunk (offset-binary, 0..15 / 0..3, or raw int8) and the activation registers of
-// one token are kept separately so that one unpack serves every token.
+// Split form of chunk_dot for the batched kernels: the unpacked weight bytes of a
+// chunk (top-bit S * w, or raw int8) and the activation registers of one token are
+// kept separately so that one unpack serves every token.
 template <int WB>
 struct Unp {
   static constexpr int N = (WB == 2) ? 16 : 8;  // dwords of unpacked weights per chunk
@@ -132,9 +135,8 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK
   if constexpr (WB == 4) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint32_t t = wq[i] ^ 0x88888888u;
-      u[i] = (int)(t & 0x0F0F0F0Fu);
-      u[4 + i] = (int)((t >> 4) & 0x0F0F0F0Fu);
+      u[i] = (int)((wq[i] << 4) & 0xF0F0F0F0u);
+      u[4 + i] = (int)(wq[i] & 0xF0F0F0F0u);
     }
   } else if constexpr (WB == 8) {
 #pragma unroll
@@ -145,22 +147,22 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK
     for (int blk = 0; blk < 2; blk++)
 #pragma unroll
       for (int h = 0; h < 2; h++) {
-        const uint32_t t = wq[2 * blk + h] ^ 0xAAAAAAAAu;
+        const uint32_t t = wq[2 * blk + h];
 #pragma unroll
-        for (int m = 0; m < 4; m++) u[8 * blk + 2 * m + h] = (int)((t >> (2 * m)) & 0x03030303u);
+        for (int m = 0; m < 4; m++) u[8 * blk + 2 * m + h] = (int)((t << (6 - 2 * m)) & 0xC0C0C0C0u);
       }
   }
 }
 
-// activation registers of one chunk for one token: Q8_0 bytes and {d, sum} per block
+// activation registers of one chunk for one token: Q8_0 bytes and d per block
 template <int WB>
 struct Act {
   int x[Unp<WB>::N];
-  int2 ds[Fmt<WB>::BPC];
+  float d[Fmt<WB>::BPC];
 };
 
 template <int WB>
-__device__ __forceinline__ void load_act(const int8_t *xa, const int2 *xd, Act<WB> &a) {
+__device__ __forceinline__ void load_act(const int8_t *xa, const float *xd, Act<WB> &a) {
 #pragma unroll
   for (int i = 0; i < Unp<WB>::N / 4; i++) {
     const int4 v = *reinterpret_cast<const int4 *>(xa + 16 * i);
@@ -170,22 +172,21 @@ __device__ __forceinline__ void load_act(const int8_t *xa, const int2 *xd, Act<W
     a.x[4 * i + 3] = v.w;
   }
 #pragma unroll
-  for (int b = 0; b < Fmt<WB>::BPC; b++) a.ds[b] = xd[b];
+  for (int b = 0; b < Fmt<WB>::BPC; b++) a.d[b] = xd[b];
 }
 
 template <int WB>
 __device__ __forceinline__ float dot_unpacked(const int (&u)[Unp<WB>::N], const Act<WB> &a) {
-  constexpr int OFF = (WB == 4) ? 8 : (WB == 2) ? 2 : 0;  // offset-binary bias of the weights
   float r = 0.0f;
 #pragma unroll
   for (int b = 0; b < Fmt<WB>::BPC; b++) {
-    int acc = -OFF * a.ds[b].y;
+    int acc = 0;
 #pragma unroll
     for (int i = 0; i < 8; i++) acc = dot4(u[8 * b + i], a.x[8 * b + i], acc);
     if (b == 0)
-      r = __int_as_float(a.ds[b].x) * (float)acc;
+      r = a.d[b] * (float)acc;
     else
-      r += __int_as_float(a.ds[b].x) * (float)acc;
+      r += a.d[b] * (float)acc;
   }
   return r;
 }
@@ -295,6 +296,65 @@ __device__ __forceinline__ int slot_pair(const FfnArgs &a, const SlotLds &L, boo
   return a.idx ? L.pairs[i] : a.perm[beg + i];
 }
 
+// Cross-lane exchanges without LDS traffic. Within an aligned group of 2*O lanes
+// the step for O pairs every lane of the lower half with one of the upper half:
+// O = 32 and 16 by the permlane swaps (v_permlane32_swap exchanges the upper 32
+// lanes of one register with the lower 32 of another, v_permlane16_swap the odd
+// 16-lane rows with the even ones), O = 8 and 4 by the DPP row mirrors (partner
+// lane l ^ 15 and l ^ 7), O = 2 and 1 by DPP quad permutes (l ^ 2, l ^ 1).
+template <int O>
+__device__ __forceinline__ float dpp_partner(float v) {
+  static_assert(O == 8 || O == 4 || O == 2 || O == 1, "DPP partner within a 16-lane row");
+  constexpr int ctrl = (O == 8) ? 0x140 : (O == 4) ? 0x141 : (O == 2) ? 0x4E : 0xB1;
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// lo, hi of every lane -> lower-half lanes get lo + partner's lo, upper-half lanes
+// hi + partner's hi
+template <int O>
+__device__ __forceinline__ float pair_sum(float lo, float hi, bool up) {
+  if constexpr (O == 32 || O == 16) {
+    const auto r = (O == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const float send = up ? lo : hi;
+    const float keep = up ? hi : lo;
+    return keep + dpp_partner<O>(send);
+  }
+}
+
+// Sum a[0..V) over the lanes of an aligned group of 2*O lanes. Scatter steps keep
+// half of the values per lane; once one value is left the remaining steps are a
+// butterfly. On return a[0..kept) hold full sums of original indices
+// base .. base + kept - 1, the same in every lane of a group of LPR >> log2(V).
+template <int V, int O>
+__device__ __forceinline__ void reduce_scatter(float *a, int lane, int &base) {
+  if constexpr (O >= 1) {
+    const bool up = (lane & O) != 0;
+    if constexpr (V > 1) {
+#pragma unroll
+      for (int i = 0; i < V / 2; i++) a[i] = pair_sum<O>(a[i], a[i + V / 2], up);
+      if (up) base += V / 2;
+      reduce_scatter<V / 2, O / 2>(a, lane, base);
+    } else {
+      a[0] = pair_sum<O>(a[0], a[0], up);
+      reduce_scatter<1, O / 2>(a, lane, base);
+    }
+  }
+}
+
+// max over aligned groups of 32 lanes (exact in any order)
+__device__ __forceinline__ float max32(float v) {
+  v = fmaxf(v, dpp_partner<8>(v));
+  v = fmaxf(v, dpp_partner<4>(v));
+  v = fmaxf(v, dpp_partner<2>(v));
+  v = fmaxf(v, dpp_partner<1>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+
 template <int WB, int LPR, int MODE>
 __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   constexpr int NT = GEMV_NT;
@@ -327,7 +387,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
 
   extern __shared__ __align__(16) char smem[];
   int8_t *xs = reinterpret_cast<int8_t *>(smem);                      // [NT][K]
-  int2 *xds = reinterpret_cast<int2 *>(smem + NT * K);                // [NT][nkb]
+  float *xds = reinterpret_cast<float *>(smem + NT * K);              // [NT][nkb]
   float *obuf = reinterpret_cast<float *>(xds + NT * nkb);            // [NT][32]
   int *orow = reinterpret_cast<int *>(obuf + NT * GEMV_ROWS);         // [NT]
 
@@ -351,7 +411,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
     __syncthreads();
     // stage activations (16 bytes per thread per step) and their block scales
     const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
-    const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+    const float *dsrc = (MODE == MODE_GATEUP) ? a.xd : a.hd;
     const int v16 = K / 16;
     for (int i = tid; i < nt * v16; i += 256) {
       const int t = i / v16, c = i % v16;
@@ -387,7 +447,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
         for (int t = 0; t < NT; t++) {
           if (t < nt) {
             const int8_t *xa = xs + t * K + kx;
-            const int2 *xd = xds + t * nkb + c * BPC;
+            const float *xd = xds + t * nkb + c * BPC;
             acc0[t] += chunk_dot<WB>(w0, xa, xd);
             if constexpr (NMAT == 2) acc1[t] += chunk_dot<WB>(w1, xa, xd);
           }
@@ -396,22 +456,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
       // reduce across the LPR lanes of the row
 #pragma unroll
       for (int t = 0; t < NT; t++) {
-#pragma unroll
-        for (int o = LPR / 2; o >= 1; o >>= 1) {
-          acc0[t] += __shfl_xor(acc0[t], o);
-          if constexpr (NMAT == 2) acc1[t] += __shfl_xor(acc1[t], o);
-        }
+        int b0 = 0;
+        reduce_scatter<1, LPR / 2>(&acc0[t], lane, b0);
+        if constexpr (NMAT == 2) reduce_scatter<1, LPR / 2>(&acc1[t], lane, b0);
       }
       if (rv && sub == 0) {
         const int rloc = wv * WROWS + rl;
-        const float s0 = sc0[r];
+        const float s0 = sc0[r] * Fmt<WB>::INV;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           if (t < nt) {
             float v;
             if constexpr (MODE == MODE_GATEUP) {
               const float g = s0 * acc0[t];
-              const float u = sc1[r] * acc1[t];
+              const float u = (sc1[r] * Fmt<WB>::INV) * acc1[t];
               v = (g / (1.0f + expf(-g))) * u;
             } else {
               v = s0 * acc0[t];
@@ -431,16 +489,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
         const int out = orow[t];
         if constexpr (MODE == MODE_GATEUP) {
           float am = fabsf(v);
-#pragma unroll
-          for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+          am = max32(am);
           const float d = am / 127.0f;
           int q = 0;
           if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
-          int sum = q;
-#pragma unroll
-          for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
           a.hq[(int64_t)out * a.F + r0 + i] = (int8_t)q;
-          if (i == 0) a.hds[(int64_t)out * (a.F / QK) + r0 / QK] = make_int2(__float_as_int(d), sum);
+          if (i == 0) a.hd[(int64_t)out * (a.F / QK) + r0 / QK] = d;
         } else {
           a.ypair[(int64_t)out * a.H + r0 + i] = v;
         }
@@ -465,36 +519,12 @@ struct cmin {
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-// Sum a[0..V) over the lanes of an aligned group of 2*O lanes. Scatter steps keep
-// half of the values per lane; once one value is left the remaining steps are a
-// plain butterfly. On return a[0..kept) hold full sums of original indices
-// base .. base + kept - 1.
-template <int V, int O>
-__device__ __forceinline__ void reduce_scatter(float *a, int lane, int &base) {
-  if constexpr (O >= 1) {
-    if constexpr (V > 1) {
-      const bool up = (lane & O) != 0;
-#pragma unroll
-      for (int i = 0; i < V / 2; i++) {
-        const float send = up ? a[i] : a[i + V / 2];
-        const float keep = up ? a[i + V / 2] : a[i];
-        a[i] = keep + __shfl_xor(send, O);
-      }
-      if (up) base += V / 2;
-      reduce_scatter<V / 2, O / 2>(a, lane, base);
-    } else {
-      a[0] += __shfl_xor(a[0], O);
-      reduce_scatter<1, O / 2>(a, lane, base);
-    }
-  }
-}
-
 struct FastCtx {
   const uint8_t *mat0, *mat1;
   int64_t rb;        // packed bytes per row
   int K, nkb;
   const int8_t *xs;  // LDS activations [ntmax][K]
-  const int2 *xds;   // LDS block scales [ntmax][nkb]
+  const float *xds;  // LDS block scales [ntmax][nkb]
   float *obuf;       // LDS results [NMAT][8][TILE]
   int r0;            // first row of the tile
 };
@@ -592,7 +622,7 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   c.K = K;
   c.nkb = nkb;
   int8_t *xs = reinterpret_cast<int8_t *>(smem);
-  int2 *xds = reinterpret_cast<int2 *>(smem + (size_t)ntmax * K);
+  float *xds = reinterpret_cast<float *>(smem + (size_t)ntmax * K);
   float *obuf = reinterpret_cast<float *>(xds + (size_t)ntmax * nkb);
   int *orow = reinterpret_cast<int *>(obuf + NMAT * 8 * TILE);
   c.xs = xs;
@@ -602,7 +632,7 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
-  const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+  const float *dsrc = (MODE == MODE_GATEUP) ? a.xd : a.hd;
 
   for (int tc = 0; tc < n; tc += ntmax) {
     const int nt = min(ntmax, n - tc);
@@ -638,27 +668,23 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
       const float *sg = sc, *su = sc + a.F;
       for (int p = tid; p < nt * TILE; p += 256) {  // one Q8_0 block of h per 32 consecutive lanes
         const int t = p / TILE, i = p % TILE, r = c.r0 + i;
-        const float g = sg[r] * obuf[(0 * 8 + t) * TILE + i];
-        const float u = su[r] * obuf[(1 * 8 + t) * TILE + i];
+        const float g = (sg[r] * Fmt<WB>::INV) * obuf[(0 * 8 + t) * TILE + i];
+        const float u = (su[r] * Fmt<WB>::INV) * obuf[(1 * 8 + t) * TILE + i];
         const float v = (g / (1.0f + expf(-g))) * u;
         float am = fabsf(v);
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        am = max32(am);
         const float d = am / 127.0f;
         int q = 0;
         if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
-        int sum = q;
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
         const int out = orow[t];
         a.hq[(int64_t)out * a.F + r] = (int8_t)q;
-        if ((i & 31) == 0) a.hds[(int64_t)out * (a.F / QK) + r / QK] = make_int2(__float_as_int(d), sum);
+        if ((i & 31) == 0) a.hd[(int64_t)out * (a.F / QK) + r / QK] = d;
       }
     } else {
       const float *sd = sc + 2 * a.F;
       for (int p = tid; p < nt * TILE; p += 256) {
         const int t = p / TILE, i = p % TILE, r = c.r0 + i;
-        a.ypair[(int64_t)orow[t] * a.H + r] = sd[r] * obuf[t * TILE + i];
+        a.ypair[(int64_t)orow[t] * a.H + r] = (sd[r] * Fmt<WB>::INV) * obuf[t * TILE + i];
       }
     }
     __syncthreads();
@@ -768,14 +794,14 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   float s0 = 0.0f, s1 = 0.0f;
   if (pt < NTC) {
     if constexpr (MODE == MODE_GATEUP) {
-      s0 = sc[r0 + pi];
-      s1 = sc[a.F + r0 + pi];
+      s0 = sc[r0 + pi] * Fmt<WB>::INV;
+      s1 = sc[a.F + r0 + pi] * Fmt<WB>::INV;
     } else {
-      s0 = sc[2 * a.F + r0 + pi];
+      s0 = sc[2 * a.F + r0 + pi] * Fmt<WB>::INV;
     }
   }
   const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
-  const int2 *dsrc = (MODE == MODE_GATEUP) ? a.xds : a.hds;
+  const float *dsrc = (MODE == MODE_GATEUP) ? a.xd : a.hd;
 
   for (int tc = 0; tc < n; tc += NTC) {
     const int nt = min(NTC, n - tc);
@@ -829,17 +855,13 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
         const float u = s1 * obuf[NMAT - 1][pt][pi];
         const float v = (g / (1.0f + expf(-g))) * u;
         float am = fabsf(v);
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        am = max32(am);
         const float d = am / 127.0f;
         int q = 0;
         if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
-        int sum = q;
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
         if (live) {
           a.hq[(int64_t)out * a.F + r] = (int8_t)q;
-          if ((pi & 31) == 0) a.hds[(int64_t)out * (a.F / QK) + r / QK] = make_int2(__float_as_int(d), sum);
+          if ((pi & 31) == 0) a.hd[(int64_t)out * (a.F / QK) + r / QK] = d;
         }
       } else {
         if (live) a.ypair[(int64_t)out * a.H + r] = s0 * obuf[0][pt][pi];
@@ -896,7 +918,7 @@ static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int 
   // per SIMD for the int4 gate/up instantiation), which matters more than reloading a
   // tile's weights from L2 for the rare expert with more than two tokens
   const int ntmax = min(2, a.T);
-  const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(int2) + (size_t)NMAT * 8 * TILE * sizeof(float) +
+  const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(float) + (size_t)NMAT * 8 * TILE * sizeof(float) +
                      16 * sizeof(int);
   dim3 grid(nrows / TILE, slots_grid.y);
   hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR>), grid, dim3(256), lds, s, a, ntmax);
@@ -932,7 +954,7 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
     if (r != hipErrorNotSupported) return r;
   }
   dim3 grid(NROWS / GEMV_ROWS, slots);
-  const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(int2) +
+  const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(float) +
                      (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
   switch (lpr) {
 #define COLI_LPR_CASE(L) \

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   }
   __syncthreads();
   const int8_t *asrc = (MODE == MF_GATEUP) ? a.xq : a.hq;
-  const int2 *dsrc = (MODE == MF_GATEUP) ? a.xds : a.hds;
+  const float *dsrc = (MODE == MF_GATEUP) ? a.xd : a.hd;
   // this thread's token pieces: piece q -> token q / (2 KC), 16-byte part q % (2 KC)
   int64_t boff[Regs::BLOADS];
 #pragma unroll
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
 #pragma unroll
     for (int j = 0; j < Regs::BLOADS; j++)
       r.b[j] = *reinterpret_cast<const uint4 *>(asrc + boff[j] + (int64_t)kb0 * QK);
-    if (dthread) r.d = __int_as_float(dsrc[doff + kb0].x);
+    if (dthread) r.d = dsrc[doff + kb0];
   };
 
   auto lstore = [&](int buf, const Regs &r) {
@@ -345,7 +345,6 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
     // the 32 rows of this Q8_0 block of h sit in lanes li and li + 32
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const float d = amax / 127.0f;
-    int sum = 0;
     uint32_t packed[4];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) {
@@ -354,17 +353,15 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       for (int j = 0; j < 4; j++) {
         int q = 0;
         if (d != 0.0f) q = (int)fminf(fmaxf(roundf(h[4 * rr + j] / d), -127.0f), 127.0f);
-        sum += q;
         pk |= (uint32_t)(q & 0xFF) << (8 * j);
       }
       packed[rr] = pk;
     }
-    sum += __shfl_xor(sum, 32);
     if (valid) {
       int8_t *hrow = a.hq + (int64_t)out_row * a.F + rbase + 4 * grp;
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) *reinterpret_cast<uint32_t *>(hrow + 8 * rr) = packed[rr];
-      if (grp == 0) a.hds[(int64_t)out_row * (a.F / QK) + rbase / QK] = make_int2(__float_as_int(d), sum);
+      if (grp == 0) a.hd[(int64_t)out_row * (a.F / QK) + rbase / QK] = d;
     }
   } else {
     if (valid) {

@@ -1,16 +1,13 @@
 // q8_0.hip — standalone Q8_0 activation quantisation (rule in q8_0_impl.h).
 //
 // Eight lanes own one block (one float4 each): fully coalesced 16-byte loads and
-// 4-byte stores. Besides q and d the kernel can emit {d, sum q} pairs, which the
-// expert GEMV kernels use for the offset-binary weight trick
-// (sum_i x_i w_i = sum_i x_i (w_i + 8) - 8 sum_i x_i).
+// 4-byte stores.
 #include "q8_0_impl.h"
 
 namespace coli {
 
 __global__ __launch_bounds__(256) void q8_0_kernel(const float *__restrict__ x, int64_t nblk,
-                                                   int8_t *__restrict__ q, float *__restrict__ d,
-                                                   int2 *__restrict__ ds) {
+                                                   int8_t *__restrict__ q, float *__restrict__ d) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t blk = gid >> 3;
   const int sub = threadIdx.x & 7;
@@ -18,21 +15,17 @@ __global__ __launch_bounds__(256) void q8_0_kernel(const float *__restrict__ x, 
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (valid) v = *reinterpret_cast<const float4 *>(x + blk * QK + sub * 4);
   uint32_t packed;
-  int sum;
-  const float dd = q8_0_block8(v, packed, sum);
+  const float dd = q8_0_block8(v, packed);
   if (!valid) return;
   *reinterpret_cast<uint32_t *>(q + blk * QK + sub * 4) = packed;
-  if (sub == 0) {
-    if (d) d[blk] = dd;
-    if (ds) ds[blk] = make_int2(__float_as_int(dd), sum);
-  }
+  if (sub == 0) d[blk] = dd;
 }
 
-hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, int2 *ds, hipStream_t s) {
+hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, hipStream_t s) {
   const int64_t nblk = rows * (int64_t)(cols / QK);
   if (nblk == 0) return hipSuccess;
   const int64_t grid = (nblk * 8 + 255) / 256;
-  hipLaunchKernelGGL(q8_0_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk, q, d, ds);
+  hipLaunchKernelGGL(q8_0_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk, q, d);
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ __device__ __forceinline__ int q8_code(float v, float d) {
 }
 
 // One block per 8 consecutive lanes, 4 values per lane (v). Returns d; writes the
-// lane's 4 codes (packed) and the block's code sum (valid in every lane of the 8).
-__device__ __forceinline__ float q8_0_block8(const float4 v, uint32_t &packed, int &sum) {
+// lane's 4 codes (packed).
+__device__ __forceinline__ float q8_0_block8(const float4 v, uint32_t &packed) {
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   a = fmaxf(a, __shfl_xor(a, 1, 8));
   a = fmaxf(a, __shfl_xor(a, 2, 8));
@@ -29,17 +29,12 @@ __device__ __forceinline__ float q8_0_block8(const float4 v, uint32_t &packed, i
   const int c0 = q8_code(v.x, d), c1 = q8_code(v.y, d), c2 = q8_code(v.z, d), c3 = q8_code(v.w, d);
   packed = (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
            ((uint32_t)(c3 & 0xFF) << 24);
-  int s = c0 + c1 + c2 + c3;
-  s += __shfl_xor(s, 1, 8);
-  s += __shfl_xor(s, 2, 8);
-  s += __shfl_xor(s, 4, 8);
-  sum = s;
   return d;
 }
 
-// A whole wavefront quantises one row of n values (n % 32 == 0): q [n], ds [n/32].
+// A whole wavefront quantises one row of n values (n % 32 == 0): q [n], d [n/32].
 __device__ __forceinline__ void q8_0_row_wave(const float *__restrict__ x, int n, int8_t *__restrict__ q,
-                                              int2 *__restrict__ ds, int lane) {
+                                              float *__restrict__ dout, int lane) {
   const int nblk = n / QK;
   const int sub = lane & 7;
 #pragma unroll 4
@@ -49,11 +44,10 @@ __device__ __forceinline__ void q8_0_row_wave(const float *__restrict__ x, int n
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) v = reinterpret_cast<const float4 *>(x)[blk * 8 + sub];
     uint32_t packed;
-    int sum;
-    const float d = q8_0_block8(v, packed, sum);
+    const float d = q8_0_block8(v, packed);
     if (valid) {
       reinterpret_cast<uint32_t *>(q)[blk * 8 + sub] = packed;
-      if (sub == 0) ds[blk] = make_int2(__float_as_int(d), sum);
+      if (sub == 0) dout[blk] = d;
     }
   }
 }

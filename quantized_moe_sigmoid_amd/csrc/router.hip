@@ -253,10 +253,10 @@ struct SelectArgs {
   const float *bias;
   int32_t *idx;
   float *w;
-  const float *x;  // quantised into xq/xds when xq != nullptr
+  const float *x;  // quantised into xq/xd when xq != nullptr
   int H;
   int8_t *xq;
-  int2 *xds;
+  float *xd;
 };
 
 constexpr int SEL_NT = 256;  // threads per token
@@ -309,11 +309,10 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (valid) v = reinterpret_cast<const float4 *>(xr)[blk * 8 + sub];
       uint32_t packed;
-      int sum;
-      const float d = q8_0_block8(v, packed, sum);
+      const float d = q8_0_block8(v, packed);
       if (valid) {
         reinterpret_cast<uint32_t *>(a.xq + (int64_t)t * a.H)[blk * 8 + sub] = packed;
-        if (sub == 0) a.xds[(int64_t)t * nblk + blk] = make_int2(__float_as_int(d), sum);
+        if (sub == 0) a.xd[(int64_t)t * nblk + blk] = d;
       }
     }
   }
@@ -454,7 +453,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.x = r.x;
   a.H = H;
   a.xq = r.xq;
-  a.xds = r.xds;
+  a.xd = r.xd;
   if (T == 0) return hipSuccess;
   if (E <= SEL_NT)
     hipLaunchKernelGGL(select_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a);
