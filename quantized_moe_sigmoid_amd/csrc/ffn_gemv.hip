@@ -28,6 +28,8 @@
 // Gate/up epilogue (fused): h = silu(g) * u in fp32, then Q8_0 of the 32 rows of
 // the tile (one block of h per token): hq int8 and hd fp32.
 // Down epilogue: y fp32 rows, written per token as 32 consecutive floats.
+#include <type_traits>
+
 #include "coli_internal.h"
 
 namespace coli {
@@ -708,10 +710,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// DIRECT (batches that hit most experts, route given): grid row y is expert y - S
-// itself, so the tile's weight loads go out together with the load of the route
-// instead of after the slot is resolved; an expert without tokens exits.
-template <int WB, int LPR, int MODE, int WR, int NTC, bool DIRECT>
+template <int WB, int LPR, int MODE, int WR, int NTC>
 __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int RPI = WAVE / LPR;
@@ -731,23 +730,7 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   __shared__ float obuf[NMAT][NTC][TILE];
   int e, n = 0, beg = 0;
   bool shared;
-  constexpr int QD = LOCAL_GROUP_MAX_P / 64;
-  int ev[QD];
-  if constexpr (DIRECT) {
-    shared = a.has_shared && blockIdx.y == 0;
-    e = shared ? a.E : (int)blockIdx.y - a.has_shared;
-    if (!shared && threadIdx.x < 64) {  // the route, issued before the weights
-      const int P = a.T * a.k;
-#pragma unroll
-      for (int i = 0; i < QD; i++) {
-        const int p = (int)threadIdx.x + 64 * i;
-        ev[i] = -1;
-        if (p < P) ev[i] = a.idx[p];
-      }
-    }
-  } else {
-    if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
-  }
+  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rs = lane / LPR, sub = lane % LPR;
@@ -760,45 +743,25 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   const uint8_t *mat1 = blob + (int64_t)a.F * rbh;
   const int r0 = blockIdx.x * TILE;
 
+  // epilogue value of this thread: token pt, row r0 + pi of the tile; its raw row
+  // scales are loaded first (1/S is applied at use, so nothing waits for them early)
+  const int pt = tid / TILE, pi = tid % TILE;
+  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  float s0 = 0.0f, s1 = 0.0f;
+  if (pt < NTC) {
+    if constexpr (MODE == MODE_GATEUP) {
+      s0 = sc[r0 + pi];
+      s1 = sc[a.F + r0 + pi];
+    } else {
+      s0 = sc[2 * a.F + r0 + pi];
+    }
+  }
   uint32_t w[R][NMAT][CW];
 #pragma unroll
   for (int j = 0; j < R; j++) {
     const int64_t roff = (int64_t)(r0 + wv * WR + j * RPI + rs) * rb + (int64_t)sub * Fmt<WB>::CHUNK;
 #pragma unroll
     for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff, w[j][m]);
-  }
-  if constexpr (DIRECT) {  // this expert's pairs, ascending, while the weights are in flight
-    if (shared) {
-      n = a.T;
-    } else {
-      if (tid < 64) {
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < QD; i++) {
-          const bool m = ev[i] == e;
-          const uint64_t b = __ballot(m);
-          if (m) SL.pairs[cnt + __popcll(b & below)] = lane + 64 * i;
-          cnt += __popcll(b);
-        }
-        if (lane == 0) SL.n = cnt;
-      }
-      lds_barrier();
-      n = SL.n;
-    }
-    if (n == 0) return;
-  }
-  // epilogue value of this thread: token pt, row r0 + pi of the tile
-  const int pt = tid / TILE, pi = tid % TILE;
-  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
-  float s0 = 0.0f, s1 = 0.0f;
-  if (pt < NTC) {
-    if constexpr (MODE == MODE_GATEUP) {
-      s0 = sc[r0 + pi] * Fmt<WB>::INV;
-      s1 = sc[a.F + r0 + pi] * Fmt<WB>::INV;
-    } else {
-      s0 = sc[2 * a.F + r0 + pi] * Fmt<WB>::INV;
-    }
   }
   const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
   const float *dsrc = (MODE == MODE_GATEUP) ? a.xd : a.hd;
@@ -851,8 +814,8 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
         if (pt == t) out = orow[t];
       if constexpr (MODE == MODE_GATEUP) {
         // a Q8_0 block of h = 32 consecutive rows = 32 consecutive threads of one token
-        const float g = s0 * obuf[0][pt][pi];
-        const float u = s1 * obuf[NMAT - 1][pt][pi];
+        const float g = s0 * (obuf[0][pt][pi] * Fmt<WB>::INV);
+        const float u = s1 * (obuf[NMAT - 1][pt][pi] * Fmt<WB>::INV);
         const float v = (g / (1.0f + expf(-g))) * u;
         float am = fabsf(v);
         am = max32(am);
@@ -864,11 +827,330 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
           if ((pi & 31) == 0) a.hd[(int64_t)out * (a.F / QK) + r / QK] = d;
         }
       } else {
-        if (live) a.ypair[(int64_t)out * a.H + r] = s0 * obuf[0][pt][pi];
+        if (live) a.ypair[(int64_t)out * a.H + r] = s0 * (obuf[0][pt][pi] * Fmt<WB>::INV);
       }
     }
     lds_barrier();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined register GEMV (decode-sized batches: the route is at hand and
+// P <= LOCAL_GROUP_MAX_P). The work is cut into units, one unit being one
+// TILE-row tile of one slot (the shared expert, or a hit expert). A grid of G
+// workgroups, about as many as are resident on the chip at once, walks them:
+// workgroup b takes units b, b + G, b + 2G, ... (a shared work counter was
+// measured slower: thousands of same-address atomics per launch serialise).
+// A workgroup lists the hit experts from the route once. Per unit:
+//  - one wavefront lists the next unit's pairs (ascending) at the top;
+//  - the next unit's weights are loaded into the tile registers as soon as the
+//    last token pass has consumed them (per half of the rows), so they are in
+//    flight during that pass's cross-lane reduction and epilogue and HBM keeps
+//    streaming while the SIMDs compute;
+//  - the activations of the next unit's first token pass are loaded during the
+//    last epilogue, so a unit's first products wait only for its weights.
+// Token passes take two tokens, the last one a single token when the count is
+// odd; no pass computes a token twice. Same arithmetic and summation tree as
+// gemv_reg_kernel. Unit i is tile i % NT of slot i / NT of the slot list
+// [shared expert] + hit experts (ascending). (Loading the first units' weights
+// before the route is read, numbering them over every expert, was measured no
+// faster: the loads of experts without tokens are wasted.)
+struct PipeLds {
+  int route[LOCAL_GROUP_MAX_P];     // expert id of pair p (-1 past P or out of range)
+  int live[1024];                   // hit experts, ascending (E <= 1024)
+  int pairs[2][LOCAL_GROUP_MAX_P];  // pair ids of the current / next unit's expert
+  int npairs[2];
+  int nlive;                        // hit experts
+  uint32_t bits[32];
+};
+
+// pairs of expert e in ascending order (one wavefront)
+__device__ __forceinline__ void pipe_list_pairs(const PipeLds &L, int e, int P, int *out, int *nout, int lane) {
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < LOCAL_GROUP_MAX_P / 64; i++) {
+    if (64 * i < P) {
+      const bool m = L.route[lane + 64 * i] == e;
+      const uint64_t b = __ballot(m);
+      if (m) out[cnt + __popcll(b & below)] = lane + 64 * i;
+      cnt += __popcll(b);
+    }
+  }
+  if (lane == 0) *nout = cnt;
+}
+
+template <int WB, int LPR, int MODE, int WR>
+__global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
+  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int RPI = WAVE / LPR;
+  constexpr int R = WR / RPI;  // rows per lane
+  constexpr int CW = Fmt<WB>::CHUNK / 4;
+  constexpr int BPC = Fmt<WB>::BPC;
+  constexpr int TILE = 4 * WR;
+  constexpr int QD = LOCAL_GROUP_MAX_P / 64;
+  constexpr int RH = (R % 2 == 0) ? R / 2 : R;  // rows per half
+  static_assert(R * RPI == WR && R * NMAT * CW <= 64, "tile weights fit in 64 registers per lane");
+  static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
+  static_assert(2 * TILE <= 192, "epilogue of two tokens on wavefronts 0..2; wavefront 3 lists pairs");
+
+  __shared__ PipeLds L;
+  __shared__ float obuf[NMAT][2][TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rs = lane / LPR, sub = lane % LPR;
+  const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
+  const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;
+  const int NT = NROWS / TILE;  // tiles per slot
+  const int nkb = K / QK;
+  const int64_t rb = row_bytes(WB, K);
+  const int64_t rbh = row_bytes(WB, a.H);
+  const int P = a.T * a.k;
+  const int hs = a.has_shared;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+
+  // Load addresses are a wave-uniform base (scalar registers) plus one per-lane
+  // 32-bit offset, so a reload in mid-flight costs no extra vector registers.
+  // Epilogue thread tid: token pt, row pi of the tile.
+  const int pt = tid / TILE, pi = tid % TILE;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const uint32_t lane_w = (uint32_t)(rs * rb + sub * Fmt<WB>::CHUNK);
+  const uint32_t lane_x = (uint32_t)(sub * BPC * QK);
+  uint32_t w[R][NMAT][CW];
+  // weights of expert e (a.E: the shared expert), tile rows r0..: rows
+  // h * RH .. h * RH + RH - 1 of the lane's tile rows (h < 0: all rows), preceded
+  // by the row scales when h <= 0 (raw: 1/S is applied at use, so nothing waits
+  // for these loads before the epilogue)
+  auto issue = [&](int e, int r0, int h, float &t0, float &t1) {
+    if (h <= 0 && pt < 2) {
+      const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+      if constexpr (MODE == MODE_GATEUP) {
+        t0 = sc[r0 + pi];
+        t1 = sc[a.F + r0 + pi];
+      } else {
+        t0 = sc[2 * a.F + r0 + pi];
+      }
+    }
+    int64_t eoff = (int64_t)e * a.blob_bytes;
+    asm volatile("" : "+s"(eoff));  // the loads stay after whatever precedes the call
+    const uint8_t *blob = a.experts + eoff;
+    const uint8_t *mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+    const uint8_t *mat1 = blob + (int64_t)a.F * rbh;
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+      if (h >= 0 && j / RH != h) continue;
+      const int64_t roff = (int64_t)(r0 + wvu * WR + j * RPI) * rb;
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff + lane_w, w[j][m]);
+    }
+  };
+
+  float s0 = 0.0f, s1 = 0.0f, s0n = 0.0f, s1n = 0.0f;
+
+  // the hit experts, ascending (wavefront 0); the route loads go out together
+  if (wv == 0) {
+    int ev[QD];
+#pragma unroll
+    for (int i = 0; i < QD; i++) {
+      const int p = lane + 64 * i;
+      ev[i] = (p < P) ? a.idx[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < QD; i++) {
+      ev[i] = ((unsigned)ev[i] < (unsigned)a.E) ? ev[i] : -1;
+      L.route[lane + 64 * i] = ev[i];
+    }
+    if (lane < 32) L.bits[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < QD; i++)
+      if (ev[i] >= 0) atomicOr(&L.bits[ev[i] >> 5], 1u << (ev[i] & 31));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    uint32_t word = (lane < 32) ? L.bits[lane] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int o = incl - c;
+    while (word) {
+      L.live[o++] = lane * 32 + __ffs((int)word) - 1;
+      word &= word - 1;
+    }
+    if (lane == 63) L.nlive = incl;
+  }
+  __syncthreads();
+  const int nlive = __builtin_amdgcn_readfirstlane(L.nlive);
+  const int total = (hs + nlive) * NT;
+  if (b >= total) return;
+  // expert of unit i (a.E: shared) and its first tile row; both wave-uniform
+  // (scalar registers, so the load addresses stay scalar bases)
+  auto unit = [&](int i, int &r0) -> int {
+    const int sl = i / NT;
+    r0 = __builtin_amdgcn_readfirstlane((i % NT) * TILE);
+    return __builtin_amdgcn_readfirstlane((sl < hs) ? a.E : L.live[sl - hs]);
+  };
+  auto list = [&](int e, int bb) {
+    if (e >= 0 && e < a.E) pipe_list_pairs(L, e, P, L.pairs[bb], &L.npairs[bb], lane);
+  };
+
+  int cur = b, nxt = G + b;
+  int r0c = 0;
+  int ec = unit(cur, r0c);
+  issue(ec, r0c, -1, s0, s1);
+  if (wv == 3) list(ec, 0);
+  lds_barrier();
+  const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
+  const float *dsrc = (MODE == MODE_GATEUP) ? a.xd : a.hd;
+  // activations (and output rows) of tokens tc, tc + 1 of expert e, pair list bb
+  Act<WB> act[2];
+  int orow[2];
+  auto load_acts = [&](int e, int bb, int tc, int cnt) {
+    const bool sh = e == a.E;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      if (t < cnt) {
+        const int i = tc + t;
+        const int p = sh ? P + i : __builtin_amdgcn_readfirstlane(L.pairs[bb][i]);
+        orow[t] = p;
+        const int64_t arow = (MODE == MODE_GATEUP) ? (sh ? i : p / a.k) : p;
+        load_act<WB>(asrc + arow * K + lane_x, dsrc + arow * nkb + sub * BPC, act[t]);
+      }
+    }
+  };
+  // first token pass of a unit, loaded a unit ahead
+  auto load_first = [&](int e, int bb) {
+    if (e < 0) return;
+    const int n = (e == a.E) ? a.T : __builtin_amdgcn_readfirstlane(L.npairs[bb]);
+    load_acts(e, bb, 0, n < 2 ? n : 2);
+  };
+  load_first(ec, 0);
+  int buf = 0;
+  for (;;) {
+    const bool has_next = nxt < total;
+    int r0n = 0;
+    const int en = has_next ? unit(nxt, r0n) : -1;
+    if (wv == 3) list(en, buf ^ 1);  // visible after this unit's first barrier
+    {
+      const bool shared = ec == a.E;
+      const int n = shared ? a.T : __builtin_amdgcn_readfirstlane(L.npairs[buf]);
+      auto pass = [&](auto ntc_tag, int tc) {
+        constexpr int NTC = decltype(ntc_tag)::value;
+        constexpr int V = RH * NMAT * NTC;  // accumulators of one half
+        constexpr int SCAT = cmin<ilog2(V), ilog2(LPR)>::v;
+        constexpr int KEPT = V >> SCAT;
+        constexpr int WMASK = (LPR >> SCAT) - 1;
+        const bool last = tc + NTC >= n;
+        if (tc > 0) load_acts(ec, buf, tc, NTC);
+        // two halves of the tile rows: products, then (last pass) the next unit's
+        // loads into the freed registers, then the half's reduction
+#pragma unroll
+        for (int h = 0; h < R / RH; h++) {
+          float acc[V];
+#pragma unroll
+          for (int i = 0; i < V; i++) acc[i] = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < RH; jj++)
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) {
+              const int j = h * RH + jj;
+#pragma unroll
+              for (int q = 0; q < CW; q++) asm volatile("" : "+v"(w[j][m][q]));
+              int uq[Unp<WB>::N];
+              unpack_chunk<WB>(w[j][m], uq);
+#pragma unroll
+              for (int t = 0; t < NTC; t++) acc[(jj * NMAT + m) * NTC + t] += dot_unpacked<WB>(uq, act[t]);
+            }
+          if (last && en >= 0) {
+            // ordered after the products: hoisted above them the loads would need
+            // a second set of tile registers
+#pragma unroll
+            for (int i = 0; i < V; i++) asm volatile("" : "+v"(acc[i]));
+            issue(en, r0n, h, s0n, s1n);
+          }
+          int base = 0;
+          reduce_scatter<V, LPR / 2>(acc, lane, base);
+          if ((lane & WMASK) == 0) {
+#pragma unroll
+            for (int i = 0; i < KEPT; i++) {
+              const int o = base + i;
+              const int t = o % NTC, m = (o / NTC) % NMAT, jj = o / (NTC * NMAT);
+              obuf[m][t][wv * WR + (h * RH + jj) * RPI + rs] = acc[i];
+            }
+          }
+        }
+        lds_barrier();
+        int out = orow[0];
+#pragma unroll
+        for (int t = 1; t < NTC; t++)
+          if (pt == t) out = orow[t];
+        if (last) load_first(en, buf ^ 1);  // the next unit's first pass, during the epilogue
+        if (pt < NTC) {
+          const int r = r0c + pi;
+          if constexpr (MODE == MODE_GATEUP) {
+            // a Q8_0 block of h = 32 consecutive rows = 32 consecutive threads of one
+            // token (obuf * 1/S is exact: s * (obuf / S) is the one rounding of s * acc)
+            const float g = s0 * (obuf[0][pt][pi] * Fmt<WB>::INV);
+            const float uv = s1 * (obuf[NMAT - 1][pt][pi] * Fmt<WB>::INV);
+            const float v = (g / (1.0f + expf(-g))) * uv;
+            const float am = max32(fabsf(v));
+            const float d = am / 127.0f;
+            int q = 0;
+            if (d != 0.0f) q = (int)fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);
+            a.hq[(int64_t)out * a.F + r] = (int8_t)q;
+            if ((pi & 31) == 0) a.hd[(int64_t)out * (a.F / QK) + r / QK] = d;
+          } else {
+            a.ypair[(int64_t)out * a.H + r] = s0 * (obuf[0][pt][pi] * Fmt<WB>::INV);
+          }
+        }
+        lds_barrier();
+      };
+      int tc = 0;
+      for (; tc + 2 <= n; tc += 2) pass(std::integral_constant<int, 2>{}, tc);
+      if (tc < n) pass(std::integral_constant<int, 1>{}, tc);
+    }
+    if (!has_next) break;
+    cur = nxt;
+    nxt += G;
+    ec = en;
+    r0c = r0n;
+    buf ^= 1;
+    s0 = s0n;
+    s1 = s1n;
+  }
+}
+
+// resident workgroups of a kernel on the current device (cached per device)
+template <typename Kern>
+static int resident_groups(Kern k, int threads) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, threads, 0) != hipSuccess) return 0;
+  const int g = (per > 0 ? per : 1) * cus;
+  if (dev < 64) cache[dev] = g;
+  return g;
+}
+
+template <int WB, int LPR, int MODE>
+static hipError_t launch_pipe(const FfnArgs &a, int nrows, hipStream_t s) {
+  constexpr int WRMAX = 64 * (WAVE / LPR) / (Fmt<WB>::CHUNK / 4);
+  constexpr int WR = (MODE == MODE_DOWN) ? (WRMAX < 16 ? WRMAX : 16) : 8;
+  constexpr int TILE = 4 * WR;
+  if (nrows % TILE) return hipErrorNotSupported;
+  auto kern = gemv_pipe_kernel<WB, LPR, MODE, WR>;
+  const int res = resident_groups(kern, 256);
+  if (res <= 0) return hipErrorNotSupported;
+  const int64_t units = (int64_t)(a.has_shared + min(a.E, a.T * a.k)) * (nrows / TILE);
+  const int grid = (int)(units < res ? units : res);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int WB, int LPR, int MODE>
@@ -883,21 +1165,11 @@ static hipError_t launch_reg(const FfnArgs &a, int nrows, int slots, hipStream_t
   // (fewer accumulators, one more wave per SIMD; measured faster for down and for
   // small batches)
   const bool dense = (int64_t)a.T * a.k >= 2 * (int64_t)a.E;  // most experts hit (about 86% or more)
-  const bool two = MODE == MODE_GATEUP && dense;
-  // grid by expert when the route is at hand and most experts are hit
-  const bool direct = dense && a.idx != nullptr;
-  const dim3 grid(nrows / TILE, direct ? a.E + a.has_shared : slots);
-  if (direct) {
-    if (two)
-      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (two)
-      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2, false>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1, false>), grid, dim3(256), 0, s, a);
-  }
+  const dim3 grid(nrows / TILE, slots);
+  if (MODE == MODE_GATEUP && dense)
+    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -938,7 +1210,11 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   constexpr int NMATC = (MODE == MODE_GATEUP) ? 2 : 1;
   if constexpr (WB != 2 && (Fmt<WB>::CHUNK / 4) * NMATC * 8 <= 64) {
     if (cpl == 1 && (lpr == 64 || lpr == 32)) {
-      hipError_t r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
+      hipError_t r = hipErrorNotSupported;
+      if (a.idx != nullptr)
+        r = (lpr == 64) ? launch_pipe<WB, 64, MODE>(a, NROWS, s) : launch_pipe<WB, 32, MODE>(a, NROWS, s);
+      if (r == hipErrorNotSupported)
+        r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
       if (r != hipErrorNotSupported) return r;
     }
   }
