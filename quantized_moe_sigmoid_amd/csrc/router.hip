@@ -30,21 +30,51 @@ namespace coli {
 constexpr int LD_TT = 16;   // token capacity
 constexpr int LD_EPW = 2;   // experts per wavefront
 
+// fp64 lane exchanges without LDS traffic, one 32-bit half at a time. Within an
+// aligned group of 2*O lanes the step for O pairs every lane of the lower half
+// with one of the upper half: O = 32 and 16 by the permlane swaps (the upper 32
+// lanes of one register with the lower 32 of another; odd 16-lane rows with even
+// ones), O = 8 and 4 by the DPP row mirrors (partner l ^ 15, l ^ 7), O = 2 and 1
+// by DPP quad permutes (l ^ 2, l ^ 1).
+template <int O>
+__device__ __forceinline__ double dpp_partner_d(double v) {
+  constexpr int ctrl = (O == 8) ? 0x140 : (O == 4) ? 0x141 : (O == 2) ? 0x4E : 0xB1;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// lower-half lanes get lo + partner's lo, upper-half lanes hi + partner's hi
+template <int O>
+__device__ __forceinline__ double pair_sum_d(double lo, double hi, bool up) {
+  if constexpr (O == 32 || O == 16) {
+    const uint64_t l = (uint64_t)__double_as_longlong(lo), h = (uint64_t)__double_as_longlong(hi);
+    const auto r0 = (O == 32) ? __builtin_amdgcn_permlane32_swap((uint32_t)l, (uint32_t)h, false, false)
+                              : __builtin_amdgcn_permlane16_swap((uint32_t)l, (uint32_t)h, false, false);
+    const auto r1 = (O == 32) ? __builtin_amdgcn_permlane32_swap((uint32_t)(l >> 32), (uint32_t)(h >> 32), false, false)
+                              : __builtin_amdgcn_permlane16_swap((uint32_t)(l >> 32), (uint32_t)(h >> 32), false, false);
+    const double a = __longlong_as_double((long long)(((uint64_t)r1[0] << 32) | r0[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)r1[1] << 32) | r0[1]));
+    return a + b;
+  } else {
+    const double send = up ? lo : hi;
+    const double keep = up ? hi : lo;
+    return keep + dpp_partner_d<O>(send);
+  }
+}
+
 template <int V, int O>
 __device__ __forceinline__ void reduce_scatter_d(double *a, int lane, int &base) {
   if constexpr (O >= 1) {
+    const bool up = (lane & O) != 0;
     if constexpr (V > 1) {
-      const bool up = (lane & O) != 0;
 #pragma unroll
-      for (int i = 0; i < V / 2; i++) {
-        const double send = up ? a[i] : a[i + V / 2];
-        const double keep = up ? a[i + V / 2] : a[i];
-        a[i] = keep + __shfl_xor(send, O);
-      }
+      for (int i = 0; i < V / 2; i++) a[i] = pair_sum_d<O>(a[i], a[i + V / 2], up);
       if (up) base += V / 2;
       reduce_scatter_d<V / 2, O / 2>(a, lane, base);
     } else {
-      a[0] += __shfl_xor(a[0], O);
+      a[0] = pair_sum_d<O>(a[0], a[0], up);
       reduce_scatter_d<1, O / 2>(a, lane, base);
     }
   }
@@ -300,6 +330,18 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   const int t = blockIdx.x, tid = threadIdx.x;
   const int E = a.E, G = a.G, k = a.k, m = E / G;
 
+  // the K-split partials of this thread's experts, loaded before the x work so
+  // that both round trips overlap (up to 8 splits in registers, the rest later)
+  constexpr int PK = 8;
+  double pv[EPT][PK];
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
+#pragma unroll
+    for (int j = 0; j < PK; j++)
+      pv[i][j] = (e < E && j < a.ksplit) ? a.part[((int64_t)j * a.T + t) * E + e] : 0.0;
+  }
+
   if (a.xq) {  // eight lanes per 32-value block
     const int nblk = a.H / QK;
     const float *xr = a.x + (int64_t)t * a.H;
@@ -326,9 +368,12 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
     if (e < E) {
       // K-split partials summed in split order; loads issued eight at a time
       double z = 0.0;
+#pragma unroll
+      for (int j = 0; j < PK; j++)
+        if (j < a.ksplit) z += pv[i][j];
       const double *pp = a.part + (int64_t)t * E + e;
       const int64_t stride = (int64_t)a.T * E;
-      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
+      for (int k0 = PK; k0 < a.ksplit; k0 += 8) {
         double v[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) v[j] = (k0 + j < a.ksplit) ? pp[(k0 + j) * stride] : 0.0;
