@@ -331,32 +331,45 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   const int E = a.E, G = a.G, k = a.k, m = E / G;
 
   // the K-split partials of this thread's experts, loaded before the x work so
-  // that both round trips overlap (up to 8 splits in registers, the rest later)
-  constexpr int PK = 8;
+  // that both round trips overlap (up to PK splits in registers, the rest later)
+  // (clamped indices: every load is valid and unconditional, so all of them go
+  // out before the first wait; values past E or ksplit are never used)
+  constexpr int PK = (EPT == 1) ? 24 : 8;
   double pv[EPT][PK];
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
-    const int e = tid + SEL_NT * i;
+    const int e = min(tid + SEL_NT * i, E - 1);
 #pragma unroll
-    for (int j = 0; j < PK; j++)
-      pv[i][j] = (e < E && j < a.ksplit) ? a.part[((int64_t)j * a.T + t) * E + e] : 0.0;
+    for (int j = 0; j < PK; j++) pv[i][j] = a.part[((int64_t)min(j, a.ksplit - 1) * a.T + t) * E + e];
   }
 
-  if (a.xq) {  // eight lanes per 32-value block
+  if (a.xq) {  // eight lanes per 32-value block; XQ blocks per thread loaded at once
+    constexpr int XQ = 8;
     const int nblk = a.H / QK;
     const float *xr = a.x + (int64_t)t * a.H;
-    for (int b0 = 0; b0 < nblk; b0 += SEL_NT / 8) {
-      const int blk = b0 + (tid >> 3), sub = tid & 7;
-      const bool valid = blk < nblk;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (valid) v = reinterpret_cast<const float4 *>(xr)[blk * 8 + sub];
-      uint32_t packed;
-      const float d = q8_0_block8(v, packed);
-      if (valid) {
-        reinterpret_cast<uint32_t *>(a.xq + (int64_t)t * a.H)[blk * 8 + sub] = packed;
-        if (sub == 0) a.xd[(int64_t)t * nblk + blk] = d;
+    const int sub = tid & 7;
+    auto chunk = [&](int b0) {
+      float4 v[XQ];
+#pragma unroll
+      for (int i = 0; i < XQ; i++) {  // clamped: blocks past nblk are quantised but not stored
+        const int blk = min(b0 + i * (SEL_NT / 8) + (tid >> 3), nblk - 1);
+        v[i] = reinterpret_cast<const float4 *>(xr)[blk * 8 + sub];
       }
-    }
+#pragma unroll
+      for (int i = 0; i < XQ; i++) {
+        if (b0 + i * (SEL_NT / 8) < nblk) {  // uniform: whole groups of eight lanes
+          const int blk = b0 + i * (SEL_NT / 8) + (tid >> 3);
+          uint32_t packed;
+          const float d = q8_0_block8(v[i], packed);
+          if (blk < nblk) {
+            reinterpret_cast<uint32_t *>(a.xq + (int64_t)t * a.H)[blk * 8 + sub] = packed;
+            if (sub == 0) a.xd[(int64_t)t * nblk + blk] = d;
+          }
+        }
+      }
+    };
+    chunk(0);  // outside the loop: its loads need not wait for the partials
+    for (int b0 = XQ * (SEL_NT / 8); b0 < nblk; b0 += XQ * (SEL_NT / 8)) chunk(b0);
   }
 
   double s[EPT], c[EPT];
