@@ -1266,21 +1266,38 @@ hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// out[t] = sum_j w[t][j] * ypair[t*k + j] (j ascending) + ypair[P + t] (shared)
+// out[t] = sum_j w[t][j] * ypair[t*k + j] (j ascending) + ypair[P + t] (shared).
+// The slots are loaded eight at a time (independent loads in flight together) and
+// added in ascending order, so the result does not depend on the batching.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ypair, const float *__restrict__ w,
                                                       int T, int k, int H, int has_shared,
                                                       float *__restrict__ out) {
+  constexpr int JB = 8;
   const int t = blockIdx.y;
   const int c4 = blockIdx.x * 256 + threadIdx.x;  // float4 column
   if (c4 * 4 >= H) return;
+  const int64_t stride = H / 4;
+  const float4 *yp = reinterpret_cast<const float4 *>(ypair + (int64_t)t * k * H) + c4;
+  const float *wt = w + (int64_t)t * k;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; j++) {
-    const float wj = w[(int64_t)t * k + j];
-    const float4 y = reinterpret_cast<const float4 *>(ypair + ((int64_t)t * k + j) * H)[c4];
-    acc.x += wj * y.x;
-    acc.y += wj * y.y;
-    acc.z += wj * y.z;
-    acc.w += wj * y.w;
+  for (int j0 = 0; j0 < k; j0 += JB) {
+    float4 y[JB];
+    float wj[JB];
+#pragma unroll
+    for (int j = 0; j < JB; j++) {  // clamped: slots past k repeat the last one and are not added
+      const int jj = min(j0 + j, k - 1);
+      y[j] = yp[jj * stride];
+      wj[j] = wt[jj];
+    }
+#pragma unroll
+    for (int j = 0; j < JB; j++) {
+      if (j0 + j < k) {
+        acc.x += wj[j] * y[j].x;
+        acc.y += wj[j] * y[j].y;
+        acc.z += wj[j] * y[j].z;
+        acc.w += wj[j] * y[j].w;
+      }
+    }
   }
   if (has_shared) {
     const float4 y = reinterpret_cast<const float4 *>(ypair + ((int64_t)T * k + t) * H)[c4];

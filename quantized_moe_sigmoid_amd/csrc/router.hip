@@ -80,9 +80,13 @@ __device__ __forceinline__ void reduce_scatter_d(double *a, int lane, int &base)
   }
 }
 
+// When xq is set, the workgroups of each K chunk also quantise that chunk of x
+// (Q8_0, 32-value blocks, eight lanes per block) from the copy staged in LDS, 32
+// blocks per workgroup, so the selection kernel has no x work left.
 template <int NI>  // float4 per lane per row: kc = 256 * NI
 __global__ __launch_bounds__(256) void logits_decode_kernel(const float *__restrict__ x, const float *__restrict__ W,
-                                                            int T, int E, int H, double *__restrict__ part) {
+                                                            int T, int E, int H, double *__restrict__ part,
+                                                            int8_t *__restrict__ xq, float *__restrict__ xd) {
   constexpr int KC = 256 * NI;
   __shared__ float4 xs[LD_TT * KC / 4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -102,6 +106,20 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(const float *__restr
     xs[i] = reinterpret_cast<const float4 *>(x + (int64_t)t * H + k0)[c];
   }
   __syncthreads();
+  if (xq) {
+    constexpr int BPT = KC / QK;  // blocks per token in this chunk
+    const int nq = T * BPT, sub = tid & 7;
+    for (int q0 = blockIdx.x * 32; q0 < nq; q0 += gridDim.x * 32) {
+      const int q = q0 + (tid >> 3);
+      if (q < nq) {  // uniform over the eight lanes of a block
+        const int t = q / BPT, b = q % BPT;
+        uint32_t packed;
+        const float d = q8_0_block8(xs[t * (KC / 4) + b * 8 + sub], packed);
+        reinterpret_cast<uint32_t *>(xq + (int64_t)t * H + k0)[b * 8 + sub] = packed;
+        if (sub == 0) xd[(int64_t)t * (H / QK) + k0 / QK + b] = d;
+      }
+    }
+  }
   double acc[LD_EPW * LD_TT];
 #pragma unroll
   for (int i = 0; i < LD_EPW * LD_TT; i++) acc[i] = 0.0;
@@ -479,12 +497,14 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   const coli_moe_cfg &c = *r.cfg;
   const int E = c.n_experts, H = c.hidden, T = r.T;
   const int ks = r.ksplit;
+  bool x_done = false;  // x quantised by the logits kernel
   if (T <= LD_TT && H % 256 == 0) {
     dim3 grid((E + 4 * LD_EPW - 1) / (4 * LD_EPW), ks);
     if (H / ks == 512)
-      hipLaunchKernelGGL(logits_decode_kernel<2>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits);
+      hipLaunchKernelGGL(logits_decode_kernel<2>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
     else
-      hipLaunchKernelGGL(logits_decode_kernel<1>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits);
+      hipLaunchKernelGGL(logits_decode_kernel<1>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
+    x_done = true;
   } else if (T <= LD_TT) {
     dim3 grid((E + 15) / 16, 1, ks);
     hipLaunchKernelGGL((logits_kernel<16, 16, 1, 1>), grid, dim3(256), 0, s, r.x, r.W, T, E, H, H / ks, r.logits);
@@ -510,7 +530,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.w = r.w;
   a.x = r.x;
   a.H = H;
-  a.xq = r.xq;
+  a.xq = x_done ? nullptr : r.xq;
   a.xd = r.xd;
   if (T == 0) return hipSuccess;
   if (E <= SEL_NT)
