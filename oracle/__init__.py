@@ -30,12 +30,13 @@ def build(force: bool = True) -> str:
 class Cfg(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32),
                 ("top_k", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32),
-                ("rsf", C.c_float), ("has_shared", C.c_int32), ("wbits", C.c_int32)]
+                ("rsf", C.c_float), ("has_shared", C.c_int32), ("wbits", C.c_int32),
+                ("scale_group", C.c_int32)]
 
 
 def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, has_shared=False, wbits=4,
-             **_ignored) -> Cfg:
-    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits)
+             scale_group=0, **_ignored) -> Cfg:
+    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group)
 
 
 _lib = None
@@ -56,7 +57,7 @@ def lib():
             "coli_ref_moe_route": [P, P, P, P, i32, P, P],
             "coli_ref_moe_route_scores": [P, P, P, P, i32, P, P, P],
             "coli_ref_moe_group": [P, P, i32, P, P, P, P, P],
-            "coli_ref_expert_ffn": [i32, i32, i32, P, P, P, P, P, P, P, P, P, P],
+            "coli_ref_expert_ffn": [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P],
             "coli_ref_moe_ffn": [P, P, P, P, i32, P, P, P],
             "coli_ref_moe_layer": [P, P, P, P, P, P, i32, P, P, P],
         }
@@ -146,8 +147,9 @@ def group(cfg: Cfg, idx):
     return cnt, off, perm, active[: nact[0]].copy()
 
 
-def expert_ffn(hidden, ffn, wbits, blob, scales, xq, xd):
-    """All intermediates of one expert on one Q8_0 row: dict of g, u, h, hq, hd, y."""
+def expert_ffn(hidden, ffn, wbits, blob, scales, xq, xd, scale_group=0):
+    """All intermediates of one expert on one Q8_0 row: dict of g, u, h, hq, hd, y.
+    scales: one per row (scale_group 0) or one per 64 inputs of a row (scale_group 64)."""
     blob = _c(blob, np.uint8)
     scales = _c(scales, np.float32)
     xq = _c(xq, np.int8)
@@ -158,7 +160,7 @@ def expert_ffn(hidden, ffn, wbits, blob, scales, xq, xd):
     hq = np.empty(ffn, np.int8)
     hd = np.empty(ffn // 32, np.float32)
     y = np.empty(hidden, np.float64)
-    _check(lib().coli_ref_expert_ffn(hidden, ffn, wbits, _p(blob), _p(scales), _p(xq), _p(xd), _p(g), _p(u),
+    _check(lib().coli_ref_expert_ffn(hidden, ffn, wbits, scale_group, _p(blob), _p(scales), _p(xq), _p(xd), _p(g), _p(u),
                                      _p(h), _p(hq), _p(hd), _p(y)), "expert_ffn")
     return dict(g=g, u=u, h=h, hq=hq, hd=hd, y=y)
 

@@ -167,6 +167,8 @@ static int cfg_ok(const coli_ref_cfg *c) {
   if (c->top_k < 1 || c->top_k > c->topk_group * (c->n_experts / c->n_group)) return 0;
   if (c->wbits != 2 && c->wbits != 4 && c->wbits != 8) return 0;
   if (c->has_shared != 0 && c->has_shared != 1) return 0;
+  if (c->scale_group != 0 && c->scale_group != 64) return 0;
+  if (c->scale_group && (c->hidden % c->scale_group || c->ffn % c->scale_group)) return 0;
   return 1;
 }
 
@@ -290,7 +292,11 @@ int coli_ref_moe_group(const coli_ref_cfg *cfg, const int32_t *topk_idx, int32_t
  *   u_f = s_up[f]   * sum_b xd_b * I_b(up row f)             (double)
  *   h_f = g_f / (1 + exp(-g_f)) * u_f, stored as fp32 (the input of Q8_0)
  *   hq, hd = Q8_0(h)
- *   y_r = s_down[r] * sum_b hd_b * I_b(down row r)           (double) */
+ *   y_r = s_down[r] * sum_b hd_b * I_b(down row r)           (double)
+ * With group scales (one per 64 inputs of a row; JustVugg/colibri README, "2. Get
+ * the model": the gs64 int4 container) the dequantised weight is s_row,grp * q, so
+ * a row's dot is sum over groups s_grp * sum_{b in grp} d_b * I_b: a 32-value
+ * block lies inside one group. */
 static int64_t block_dot(const int8_t *a, const int8_t *b) {
   int64_t acc = 0;
   for (int i = 0; i < QK; i++) acc += (int64_t)a[i] * (int64_t)b[i];
@@ -304,13 +310,28 @@ static double row_dot(const int8_t *wrow, const int8_t *aq, const float *ad, int
   return acc;
 }
 
-int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, const uint8_t *blob,
+/* The scaled dot of one row: s[0] * row_dot with one scale per row (gs = 0), else
+ * sum over the n / gs groups of s[grp] * (the row_dot of that group's inputs). */
+static double scaled_row_dot(const int8_t *wrow, const int8_t *aq, const float *ad, int32_t n, int32_t gs,
+                             const float *s) {
+  if (gs == 0) return (double)s[0] * row_dot(wrow, aq, ad, n);
+  double acc = 0.0;
+  for (int32_t grp = 0; grp < n / gs; grp++)
+    acc += (double)s[grp] * row_dot(wrow + (int64_t)grp * gs, aq + (int64_t)grp * gs, ad + grp * (gs / QK), gs);
+  return acc;
+}
+
+int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scale_group, const uint8_t *blob,
                         const float *scales, const int8_t *xq, const float *xd,
                         double *g_out, double *u_out, float *h_out, int8_t *hq_out, float *hd_out,
                         double *y_out) {
   const int64_t rh = coli_ref_row_bytes(wbits, hidden), rf = coli_ref_row_bytes(wbits, ffn);
   if (rh < 0 || rf < 0 || !blob || !scales || !xq || !xd) return -1;
-  const int32_t H = hidden, F = ffn;
+  if (scale_group != 0 && (scale_group != 64 || hidden % 64 || ffn % 64)) return -1;
+  const int32_t H = hidden, F = ffn, gs = scale_group;
+  /* scales of one row of each matrix: per-row index, or [row][group] */
+  const int64_t sgh = gs ? H / gs : 1, sgf = gs ? F / gs : 1;
+  const float *sg = scales, *su = scales + (int64_t)F * sgh, *sd = scales + 2 * (int64_t)F * sgh;
   int8_t *wrow = malloc((size_t)(H > F ? H : F));
   float *h = malloc(sizeof(float) * (size_t)F);
   int8_t *hq = malloc((size_t)F);
@@ -322,9 +343,9 @@ int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, const uint8_
   const uint8_t *gate = blob, *up = blob + (int64_t)F * rh, *down = blob + 2 * (int64_t)F * rh;
   for (int32_t f = 0; f < F; f++) {
     coli_ref_unpack(wbits, gate + (int64_t)f * rh, H, wrow);
-    double g = (double)scales[f] * row_dot(wrow, xq, xd, H);
+    double g = scaled_row_dot(wrow, xq, xd, H, gs, sg + f * sgh);
     coli_ref_unpack(wbits, up + (int64_t)f * rh, H, wrow);
-    double u = (double)scales[F + f] * row_dot(wrow, xq, xd, H);
+    double u = scaled_row_dot(wrow, xq, xd, H, gs, su + f * sgh);
     h[f] = (float)(g / (1.0 + exp(-g)) * u);
     if (g_out) g_out[f] = g;
     if (u_out) u_out[f] = u;
@@ -333,7 +354,7 @@ int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, const uint8_
   if (y_out)
     for (int32_t r = 0; r < H; r++) {
       coli_ref_unpack(wbits, down + (int64_t)r * rf, F, wrow);
-      y_out[r] = (double)scales[2 * F + r] * row_dot(wrow, hq, hd, F);
+      y_out[r] = scaled_row_dot(wrow, hq, hd, F, gs, sd + r * sgf);
     }
   if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)F);
   if (hq_out) memcpy(hq_out, hq, (size_t)F);
@@ -356,7 +377,8 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
   if (!x || !topk_idx || !topk_w || !out) return -1;
   const int32_t H = cfg->hidden, F = cfg->ffn, k = cfg->top_k, E = cfg->n_experts;
   const int64_t blob = coli_ref_blob_bytes(H, F, cfg->wbits);
-  const int64_t srow = 2 * (int64_t)F + H;
+  const int32_t gs = cfg->scale_group;
+  const int64_t srow = gs ? 3 * (int64_t)F * (H / gs) : 2 * (int64_t)F + H;  /* scales per expert */
   for (int64_t p = 0; p < (int64_t)T * k; p++)
     if (topk_idx[p] < 0 || topk_idx[p] >= E) return -2;
   const int nslot = k + (cfg->has_shared ? 1 : 0);
@@ -375,7 +397,7 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
         coli_ref_quantize_q8_0(x + (int64_t)t * H, 1, H, xq, xd);
         for (int j = 0; j < nslot; j++) {
           int64_t e = j < k ? topk_idx[(int64_t)t * k + j] : E; /* shared expert stored after the routed ones */
-          coli_ref_expert_ffn(H, F, cfg->wbits, experts + e * blob, scales + e * srow, xq, xd, NULL, NULL,
+          coli_ref_expert_ffn(H, F, cfg->wbits, gs, experts + e * blob, scales + e * srow, xq, xd, NULL, NULL,
                               NULL, NULL, NULL, y + (int64_t)j * H);
         }
         for (int32_t r = 0; r < H; r++) {

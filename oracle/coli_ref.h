@@ -47,6 +47,7 @@ typedef struct {
   float   rsf;          /* routed_scaling_factor */
   int32_t has_shared;   /* 0/1: shared expert stored after the routed ones */
   int32_t wbits;        /* 2, 4 or 8 */
+  int32_t scale_group;  /* 0: one fp32 scale per row; 64: one per 64 consecutive inputs of a row */
 } coli_ref_cfg;
 
 /* Q8_0 of rows x cols fp32 values (cols % 32 == 0): q int8 [rows, cols], d fp32 [rows, cols/32]. */
@@ -74,10 +75,12 @@ int coli_ref_moe_group(const coli_ref_cfg *cfg, const int32_t *topk_idx, int32_t
                        int32_t *pair_perm /*[T*k]*/, int32_t *active /*[E]*/, int32_t *n_active);
 
 /* One expert applied to one Q8_0 activation row, with every intermediate.
- * blob: gate[F] | up[F] | down[H] packed rows; scales: fp32 [2F + H].
+ * blob: gate[F] | up[F] | down[H] packed rows. scales (fp32): with scale_group 0,
+ * [2F + H] one per row (gate rows, up rows, down rows); with scale_group 64, one
+ * per 64 inputs of a row, gate [F][H/64] | up [F][H/64] | down [H][F/64].
  * Outputs (any may be NULL): g, u double [F]; h fp32 [F]; hq int8 [F];
  * hd fp32 [F/32]; y double [H]. */
-int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, const uint8_t *blob,
+int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scale_group, const uint8_t *blob,
                         const float *scales, const int8_t *xq, const float *xd,
                         double *g, double *u, float *h, int8_t *hq, float *hd, double *y);
 

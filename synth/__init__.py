@@ -124,10 +124,16 @@ def expert_blob(seed: int, layer: int, expert: int, hidden: int, ffn: int, wbits
     return b
 
 
-def expert_scales(seed: int, layer: int, expert: int, hidden: int, ffn: int) -> np.ndarray:
-    """Per-row fp32 scales of one expert, U(0.005, 0.02): gate[F], up[F], down[H]."""
+def scales_per_expert(hidden: int, ffn: int, scale_group: int = 0) -> int:
+    """fp32 scales of one expert: one per row, or one per scale_group inputs of a row."""
+    return 2 * ffn + hidden if scale_group == 0 else 3 * ffn * (hidden // scale_group)
+
+
+def expert_scales(seed: int, layer: int, expert: int, hidden: int, ffn: int, scale_group: int = 0) -> np.ndarray:
+    """fp32 scales of one expert, U(0.005, 0.02): per row gate[F], up[F], down[H]; or with
+    group scales gate[F][H/g], up[F][H/g], down[H][F/g]."""
     key = derive_key(seed, TAG_SCALE, layer, expert)
-    u = uniform01(key, 2 * ffn + hidden)
+    u = uniform01(key, scales_per_expert(hidden, ffn, scale_group))
     return (0.005 + 0.015 * u).astype(np.float32)
 
 
@@ -163,14 +169,14 @@ def zipf_bias(seed: int, layer: int, n_experts: int, s: float = 1.1, beta: float
 
 def layer_inputs(seed: int, layer: int, *, tokens: int, hidden: int, ffn: int, n_experts: int,
                  has_shared: bool, wbits: int, zipf: bool = False, with_blobs: bool = True,
-                 x_index: int = 0) -> dict:
+                 x_index: int = 0, scale_group: int = 0) -> dict:
     """All host-side inputs of one layer. Blobs are [E+S, blob_bytes] uint8."""
     ne = n_experts + (1 if has_shared else 0)
     d = {
         "x": activations(seed, layer, tokens, hidden, x_index),
         "router_w": router_weight(seed, layer, n_experts, hidden),
         "router_bias": zipf_bias(seed, layer, n_experts) if zipf else router_bias(seed, layer, n_experts),
-        "scales": np.stack([expert_scales(seed, layer, e, hidden, ffn) for e in range(ne)]),
+        "scales": np.stack([expert_scales(seed, layer, e, hidden, ffn, scale_group) for e in range(ne)]),
     }
     if with_blobs:
         d["blobs"] = np.stack([expert_blob(seed, layer, e, hidden, ffn, wbits) for e in range(ne)])

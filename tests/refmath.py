@@ -31,15 +31,23 @@ def row_bytes(n, wbits):
     return n * wbits // 8
 
 
-def dequant_expert(blob, scales, hidden, ffn, wbits):
-    """Dense float64 gate, up [F, H] and down [H, F] matrices: scale[row] * q."""
+def dequant_expert(blob, scales, hidden, ffn, wbits, scale_group=0):
+    """Dense float64 gate, up [F, H] and down [H, F] matrices: scale[row] * q, or with
+    group scales scale[row][input // scale_group] * q (scales gate[F][H/g], up, down[H][F/g])."""
     rh, rf = row_bytes(hidden, wbits), row_bytes(ffn, wbits)
     blob = np.asarray(blob, np.uint8)
     gate = unpack_np(blob[: ffn * rh], wbits, ffn * hidden).reshape(ffn, hidden)
     up = unpack_np(blob[ffn * rh: 2 * ffn * rh], wbits, ffn * hidden).reshape(ffn, hidden)
     down = unpack_np(blob[2 * ffn * rh: 2 * ffn * rh + hidden * rf], wbits, hidden * ffn).reshape(hidden, ffn)
     s = np.asarray(scales, np.float64)
-    return (gate * s[:ffn, None], up * s[ffn: 2 * ffn, None], down * s[2 * ffn:, None])
+    if scale_group == 0:
+        return (gate * s[:ffn, None], up * s[ffn: 2 * ffn, None], down * s[2 * ffn:, None])
+    g = scale_group
+    ng, nd = ffn * (hidden // g), hidden * (ffn // g)
+    sg = np.repeat(s[:ng].reshape(ffn, hidden // g), g, axis=1)
+    su = np.repeat(s[ng: 2 * ng].reshape(ffn, hidden // g), g, axis=1)
+    sd = np.repeat(s[2 * ng: 2 * ng + nd].reshape(hidden, ffn // g), g, axis=1)
+    return (gate * sg, up * su, down * sd)
 
 
 def dequant_q8(q, d):

@@ -143,3 +143,49 @@ def test_layer_ffn_matches_route_then_ffn(oracle_lib):
     idx2, w2 = oracle_lib.route(cfg, inp["router_w"], inp["router_bias"], inp["x"])
     assert np.array_equal(idx, idx2) and np.array_equal(w, w2)
     assert np.array_equal(out, oracle_lib.ffn(cfg, inp["blobs"], inp["scales"], inp["x"], idx, w))
+
+
+@pytest.mark.parametrize("wbits", [4, 8, 2])
+def test_expert_ffn_group_scales_vs_dense_double(oracle_lib, wbits):
+    """One scale per 64 inputs of a row (the gs64 container): the per-block integer
+    dots scaled by block and group scales equal a dense float64 product of the
+    dequantised operands, s[row][i // 64] * q[row][i]."""
+    H, F = 192, 128
+    inp = synth.layer_inputs(78, 0, tokens=4, hidden=H, ffn=F, n_experts=2, has_shared=False, wbits=wbits,
+                             scale_group=64)
+    assert inp["scales"].shape == (2, 3 * F * H // 64)
+    xq, xd = oracle_lib.quantize_q8_0(inp["x"])
+    for e in range(2):
+        blob, sc = inp["blobs"][e], inp["scales"][e]
+        Wg, Wu, Wd = refmath.dequant_expert(blob, sc, H, F, wbits, scale_group=64)
+        for t in range(4):
+            r = oracle_lib.expert_ffn(H, F, wbits, blob, sc, xq[t], xd[t], scale_group=64)
+            xhat = refmath.dequant_q8(xq[t], xd[t])
+            g, u = Wg @ xhat, Wu @ xhat
+            assert np.allclose(r["g"], g, rtol=1e-12, atol=1e-12 * np.abs(g).max())
+            assert np.allclose(r["u"], u, rtol=1e-12, atol=1e-12 * np.abs(u).max())
+            y = Wd @ refmath.dequant_q8(r["hq"], r["hd"])
+            assert np.allclose(r["y"], y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def test_group_scales_equal_to_row_scale_reduce_to_per_row(oracle_lib):
+    """Group scales that repeat each row's scale give the per-row expert."""
+    H, F = 128, 64
+    inp = synth.layer_inputs(79, 0, tokens=3, hidden=H, ffn=F, n_experts=1, has_shared=False, wbits=4)
+    blob, sr = inp["blobs"][0], inp["scales"][0]
+    sg = np.concatenate([np.repeat(sr[:F], H // 64), np.repeat(sr[F:2 * F], H // 64), np.repeat(sr[2 * F:], F // 64)])
+    xq, xd = oracle_lib.quantize_q8_0(inp["x"])
+    for t in range(3):
+        a = oracle_lib.expert_ffn(H, F, 4, blob, sr, xq[t], xd[t])
+        b = oracle_lib.expert_ffn(H, F, 4, blob, sg, xq[t], xd[t], scale_group=64)
+        for key in ("g", "u", "y"):
+            assert np.allclose(a[key], b[key], rtol=1e-13, atol=1e-13 * np.abs(a[key]).max())
+
+
+def test_layer_group_scales_rejects_bad_group(oracle_lib):
+    """Only 0 (per row) and 64 are group sizes; 64 must divide H and F."""
+    inp = synth.layer_inputs(80, 0, tokens=2, hidden=96, ffn=64, n_experts=2, has_shared=False, wbits=4)
+    for gs, H in ((32, 128), (64, 96)):
+        cfg = oracle_lib.make_cfg(hidden=H, ffn=64, n_experts=2, top_k=1, wbits=4, scale_group=gs)
+        with pytest.raises(ValueError):
+            oracle_lib.layer(cfg, inp["blobs"], inp["scales"], inp["router_w"], inp["router_bias"], inp["x"])
