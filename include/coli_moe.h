@@ -33,13 +33,19 @@
  *                a blob is gate[F rows] | up[F rows] | down[H rows] of packed rows;
  *                gate and up rows have H inputs, down rows have F inputs.
  *                The shared expert, when present, is blob E.
- *   scales       fp32 [(E + has_shared)][2F + H]: gate rows, up rows, down rows.
+ *   scales       fp32, per expert (scale_group 0) [2F + H]: one per row, gate rows,
+ *                up rows, down rows; or (scale_group 64) [3 F H / 64]: one per 64
+ *                consecutive inputs of a row, gate [F][H/64] | up [F][H/64] |
+ *                down [H][F/64]. Expert i's scales start at i * coli_moe_scales_per_expert.
+ *                (Group scales: JustVugg/colibri README, "2. Get the model", the gs64
+ *                int4 container; the pages fix neither the scale type nor the layout,
+ *                this library reads them as fp32 in that order.)
  *   router_w     fp32 [E][H];  router_bias fp32 [E] (noaux_tc correction bias).
  *   Packed row of n inputs = n/32 blocks of 32 values, two's complement:
  *     int8 (wfmt 8): 32 bytes/block, byte i = value i;
  *     int4 (wfmt 4): 16 bytes/block, byte j = value j | value (j+16) << 4;
  *     int2 (wfmt 2):  8 bytes/block, byte j = sum_m value (j+8m) << 2m, m = 0..3.
- *   Dequantised weight = scale[row] * value.
+ *   Dequantised weight = scale[row] * value, or scale[row][input / 64] * value.
  *
  * Numerics (the readings):
  *   Q8_0: per 32-value block d = max|x| / 127 (one fp32 division, stored fp32),
@@ -50,7 +56,8 @@
  *     the Gk best groups kept; the k best c inside them are the route, in
  *     descending order; every tie goes to the lower index;
  *     w_j = (float)(s_j / sum_j s_j * rsf), the sum taken in slot order.
- *   Expert (SwiGLU): g = s_gate * sum_b xd_b * I_b, u likewise with the up rows,
+ *   Expert (SwiGLU): g = s_gate * sum_b xd_b * I_b (group scales: sum_b s_gate,b/2 *
+ *     xd_b * I_b, a 32-value block lying inside one group), u likewise with the up rows,
  *     where I_b is the exact int32 dot of block b; h = silu(g) * u in fp32;
  *     hq, hd = Q8_0(h); y = s_down * sum_b hd_b * I_b(hq, down row).
  *   Combine: out_t = sum_j w_tj * y_{e_tj} (j = 0..k-1 in order) + y_shared, fp32,
@@ -80,7 +87,7 @@ typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8 } coli_wfmt;
 /* Layer shape. Limits: hidden and ffn multiples of 128; 1 <= n_experts <= 1024;
  * n_experts % n_group == 0; 1 <= topk_group <= n_group <= 64;
  * 1 <= top_k <= min(64, topk_group * n_experts / n_group); has_shared 0 or 1;
- * wfmt 2, 4 or 8. */
+ * wfmt 2, 4 or 8; scale_group 0 or 64. */
 typedef struct {
   int32_t hidden;               /* H */
   int32_t ffn;                  /* F, width of every expert (shared included) */
@@ -91,6 +98,7 @@ typedef struct {
   float routed_scaling_factor;  /* rsf */
   int32_t has_shared;           /* 1: blob E is a shared expert applied to every token */
   int32_t wfmt;                 /* coli_wfmt, one format for all experts of the layer */
+  int32_t scale_group;          /* 0: one scale per weight row; 64: one per 64 inputs of a row */
 } coli_moe_cfg;
 
 /* Device weights of one layer. experts: 16-byte aligned; router_w: 16-byte aligned;
@@ -104,6 +112,10 @@ typedef struct {
 
 /* Bytes of one packed expert blob (0 if cfg is invalid). */
 size_t coli_moe_blob_bytes(const coli_moe_cfg *cfg);
+
+/* fp32 scales of one expert: 2F + H (scale_group 0) or 3 F H / 64 (scale_group 64);
+ * 0 if cfg is invalid. */
+size_t coli_moe_scales_per_expert(const coli_moe_cfg *cfg);
 
 /* Workspace bytes that coli_moe_route / coli_moe_ffn / coli_moe_layer need for
  * up to T_max tokens (0 if cfg is invalid or T_max out of range). T_max * top_k

@@ -32,7 +32,7 @@ class Cfg(C.Structure):
     """coli_moe_cfg."""
     _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("n_group", C.c_int32), ("topk_group", C.c_int32), ("routed_scaling_factor", C.c_float),
-                ("has_shared", C.c_int32), ("wfmt", C.c_int32)]
+                ("has_shared", C.c_int32), ("wfmt", C.c_int32), ("scale_group", C.c_int32)]
 
 
 class _Weights(C.Structure):
@@ -41,13 +41,13 @@ class _Weights(C.Structure):
 
 
 def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, has_shared=False, wbits=4,
-             **_ignored) -> Cfg:
-    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits)
+             scale_group=0, **_ignored) -> Cfg:
+    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group)
 
 
 @dataclass
 class Weights:
-    """Device tensors of one layer: experts uint8 [(E+S) * blob], scales fp32 [(E+S), 2F+H],
+    """Device tensors of one layer: experts uint8 [(E+S) * blob], scales fp32 [(E+S), scales_per_expert],
     router_w fp32 [E, H], router_bias fp32 [E]."""
     experts: object
     scales: object
@@ -62,6 +62,7 @@ _lib = None
 
 EXPORTS = {
     "coli_moe_blob_bytes": (C.c_size_t, [C.c_void_p]),
+    "coli_moe_scales_per_expert": (C.c_size_t, [C.c_void_p]),
     "coli_moe_workspace_bytes": (C.c_size_t, [C.c_void_p, C.c_int32]),
     "coli_moe_quantize_q8_0": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "coli_moe_route": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
@@ -131,6 +132,10 @@ def strerror(status: int) -> str:
 
 def blob_bytes(cfg: Cfg) -> int:
     return int(lib().coli_moe_blob_bytes(C.byref(cfg)))
+
+
+def scales_per_expert(cfg: Cfg) -> int:
+    return int(lib().coli_moe_scales_per_expert(C.byref(cfg)))
 
 
 def workspace_bytes(cfg: Cfg, T_max: int) -> int:

@@ -59,6 +59,8 @@ struct FfnArgs {
   const uint8_t *experts;
   const float *scales;
   int64_t blob_bytes;
+  int64_t scale_stride;  // fp32 scales per expert
+  int32_t gs;            // 0: one scale per row; 64: one per 64 inputs of a row
   int32_t H, F, E, k, T, has_shared;
   const int32_t *off, *perm, *active, *nact;  // grouping arrays (read when idx == nullptr)
   const int32_t *idx;  // route [T][k]: each workgroup groups locally when set (T*k <= LOCAL_GROUP_MAX_P)

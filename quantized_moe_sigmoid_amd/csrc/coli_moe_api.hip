@@ -50,6 +50,7 @@ static int check_cfg(const coli_moe_cfg *c) {
   if (c->n_experts % c->n_group || c->topk_group > c->n_group) return COLI_E_INVALID;
   if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return COLI_E_INVALID;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return COLI_E_INVALID;  // NaN
+  if (c->scale_group != 0 && c->scale_group != 64) return COLI_E_INVALID;
   if (c->hidden % 128 || c->ffn % 128) return COLI_E_UNSUPPORTED;
   if (c->n_experts > 1024 || c->n_group > 64 || c->top_k > 64) return COLI_E_UNSUPPORTED;
   if (gemv_lds(c->hidden) > GEMV_LDS_LIMIT || gemv_lds(c->ffn) > GEMV_LDS_LIMIT) return COLI_E_UNSUPPORTED;
@@ -100,6 +101,8 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.experts = static_cast<const uint8_t *>(w.experts);
   a.scales = w.scales;
   a.blob_bytes = coli_moe_blob_bytes(&c);
+  a.scale_stride = coli_moe_scales_per_expert(&c);
+  a.gs = c.scale_group;
   a.H = c.hidden;
   a.F = c.ffn;
   a.E = c.n_experts;
@@ -189,6 +192,12 @@ size_t coli_moe_blob_bytes(const coli_moe_cfg *cfg) {
   if (check_cfg(cfg) != COLI_OK) return 0;
   return (size_t)(2 * (int64_t)cfg->ffn * row_bytes(cfg->wfmt, cfg->hidden) +
                   (int64_t)cfg->hidden * row_bytes(cfg->wfmt, cfg->ffn));
+}
+
+size_t coli_moe_scales_per_expert(const coli_moe_cfg *cfg) {
+  if (check_cfg(cfg) != COLI_OK) return 0;
+  const int64_t H = cfg->hidden, F = cfg->ffn;
+  return (size_t)(cfg->scale_group ? 3 * F * (H / cfg->scale_group) : 2 * F + H);
 }
 
 size_t coli_moe_workspace_bytes(const coli_moe_cfg *cfg, int32_t T_max) {

@@ -357,7 +357,9 @@ __device__ __forceinline__ float max32(float v) {
 }
 
 
-template <int WB, int LPR, int MODE>
+// GS: one scale per 64 inputs of a row (the scale of a chunk's group multiplies the
+// chunk's contribution; a chunk never straddles two groups) instead of one per row.
+template <int WB, int LPR, int MODE, bool GS = false>
 __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   constexpr int NT = GEMV_NT;
   constexpr int RPI = WAVE / LPR;        // rows per wave iteration
@@ -383,9 +385,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   const int64_t rbh = row_bytes(WB, a.H);
   const uint8_t *mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
   const uint8_t *mat1 = blob + (int64_t)a.F * rbh;  // up (gate/up mode only)
-  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  const float *sc = a.scales + (int64_t)e * a.scale_stride;
   const float *sc0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * a.F;
   const float *sc1 = sc + a.F;
+  // group scales: gate [F][H/64] | up [F][H/64] | down [H][F/64]
+  const int64_t ngh = (int64_t)a.F * (a.H / 64);
+  const float *gsc0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * ngh;
+  const float *gsc1 = sc + ngh;
 
   extern __shared__ __align__(16) char smem[];
   int8_t *xs = reinterpret_cast<int8_t *>(smem);                      // [NT][K]
@@ -445,13 +451,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
         load_chunk<WB>(p0 + (int64_t)c * Fmt<WB>::CHUNK, w0);
         if constexpr (NMAT == 2) load_chunk<WB>(p1 + (int64_t)c * Fmt<WB>::CHUNK, w1);
         const int kx = c * BPC * QK;  // first input of this chunk
+        float g0 = 1.0f, g1 = 1.0f;
+        if constexpr (GS) {
+          const int64_t gi = (int64_t)r * (K / 64) + kx / 64;
+          g0 = gsc0[gi];
+          if constexpr (NMAT == 2) g1 = gsc1[gi];
+        }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           if (t < nt) {
             const int8_t *xa = xs + t * K + kx;
             const float *xd = xds + t * nkb + c * BPC;
-            acc0[t] += chunk_dot<WB>(w0, xa, xd);
-            if constexpr (NMAT == 2) acc1[t] += chunk_dot<WB>(w1, xa, xd);
+            if constexpr (GS) {
+              acc0[t] = fmaf(g0, chunk_dot<WB>(w0, xa, xd), acc0[t]);
+              if constexpr (NMAT == 2) acc1[t] = fmaf(g1, chunk_dot<WB>(w1, xa, xd), acc1[t]);
+            } else {
+              acc0[t] += chunk_dot<WB>(w0, xa, xd);
+              if constexpr (NMAT == 2) acc1[t] += chunk_dot<WB>(w1, xa, xd);
+            }
           }
         }
       }
@@ -464,14 +481,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
       }
       if (rv && sub == 0) {
         const int rloc = wv * WROWS + rl;
-        const float s0 = sc0[r] * Fmt<WB>::INV;
+        const float s0 = (GS ? 1.0f : sc0[r]) * Fmt<WB>::INV;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           if (t < nt) {
             float v;
             if constexpr (MODE == MODE_GATEUP) {
               const float g = s0 * acc0[t];
-              const float u = (sc1[r] * Fmt<WB>::INV) * acc1[t];
+              const float u = ((GS ? 1.0f : sc1[r]) * Fmt<WB>::INV) * acc1[t];
               v = (g / (1.0f + expf(-g))) * u;
             } else {
               v = s0 * acc0[t];
@@ -614,7 +631,7 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   const int nkb = K / QK;
   const uint8_t *blob = a.experts + (int64_t)e * a.blob_bytes;
   const int64_t rbh = row_bytes(WB, a.H);
-  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  const float *sc = a.scales + (int64_t)e * a.scale_stride;
 
   extern __shared__ __align__(16) char smem[];
   FastCtx c;
@@ -746,7 +763,7 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
   // epilogue value of this thread: token pt, row r0 + pi of the tile; its raw row
   // scales are loaded first (1/S is applied at use, so nothing waits for them early)
   const int pt = tid / TILE, pi = tid % TILE;
-  const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+  const float *sc = a.scales + (int64_t)e * a.scale_stride;
   float s0 = 0.0f, s1 = 0.0f;
   if (pt < NTC) {
     if constexpr (MODE == MODE_GATEUP) {
@@ -922,7 +939,7 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
   // for these loads before the epilogue)
   auto issue = [&](int e, int r0, int h, float &t0, float &t1) {
     if (h <= 0 && pt < 2) {
-      const float *sc = a.scales + (int64_t)e * (2 * a.F + a.H);
+      const float *sc = a.scales + (int64_t)e * a.scale_stride;
       if constexpr (MODE == MODE_GATEUP) {
         t0 = sc[r0 + pi];
         t1 = sc[a.F + r0 + pi];
@@ -1206,6 +1223,26 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   const int lpr = pick_lpr(nchunk);
   const int cpl = nchunk / lpr;
   const int slots = a.has_shared + min(a.E, a.T * a.k);
+  if (a.gs != 0) {  // group scales: the generic kernel
+    dim3 grid(NROWS / GEMV_ROWS, slots);
+    const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(float) +
+                       (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
+    if (a.gs != 64 || K % 64) return hipErrorInvalidValue;
+    switch (lpr) {
+#define COLI_LPR_CASE(L) \
+  case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE, true>), grid, dim3(256), lds, s, a); break;
+      COLI_LPR_CASE(64)
+      COLI_LPR_CASE(32)
+      COLI_LPR_CASE(16)
+      COLI_LPR_CASE(8)
+      COLI_LPR_CASE(4)
+      COLI_LPR_CASE(2)
+      COLI_LPR_CASE(1)
+#undef COLI_LPR_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // one chunk per lane and row, and the tile fits in registers: weights stay resident
   constexpr int NMATC = (MODE == MODE_GATEUP) ? 2 : 1;
   if constexpr (WB != 2 && (Fmt<WB>::CHUNK / 4) * NMATC * 8 <= 64) {

@@ -107,6 +107,7 @@ struct MfLds {
   int8_t a[2][NMAT][MF_ROWS][ROWB];
   int8_t b[2][MF_TOK][ROWB];
   float d[2][MF_TOK][KC];  // block scale of each token
+  __attribute__((aligned(16))) float gs[2][NMAT][KC * QK / 64][MF_ROWS];  // group scales of the stage's rows
 };
 
 enum { MF_GATEUP = 0, MF_DOWN = 1 };
@@ -123,10 +124,14 @@ struct MfRegs {
   uint4 a[ALOADS];
   uint4 b[BLOADS];
   float d;
+  float gs;
 };
 
 // ------------------------------------------------------------------ GEMM
-template <int WB, int MODE, int KC>
+// GS: one scale per 64 inputs of a row (group scales): each block's scale is then
+// d_b * s(row, group of b), applied per result; otherwise one scale per row, applied
+// in the epilogue.
+template <int WB, int MODE, int KC, bool GS>
 __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__restrict__ tiles,
                                                    const int32_t *__restrict__ ntiles, int gmax, int nf) {
   constexpr int NMAT = (MODE == MF_GATEUP) ? 2 : 1;
@@ -191,6 +196,18 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   }
   const bool dthread = tid < MF_TOK * KC;
   const int64_t doff = (int64_t)act_rows[dthread ? tid / KC : 0] * nkb + tid % KC;
+  // group scales of a stage: NMAT x (KC / 2) groups x 64 rows, one per thread;
+  // thread q -> matrix q / (NG * 64), group (q / 64) % NG, row q % 64
+  constexpr int NG = KC * QK / 64;
+  const bool gthread = GS && tid < NMAT * NG * MF_ROWS;
+  const float *gsrc = nullptr;
+  if constexpr (GS) {
+    const int sc_m = tid / (NG * MF_ROWS), sc_row = r0 + tid % MF_ROWS;
+    const int64_t ngh = (int64_t)a.F * (a.H / 64);
+    const float *base = a.scales + (int64_t)ti.x * a.scale_stride +
+                        ((MODE == MF_GATEUP) ? (sc_m == 1 ? ngh : 0) : 2 * ngh);
+    gsrc = base + (int64_t)sc_row * (K / 64) + (tid / MF_ROWS) % NG;
+  }
 
   auto gload = [&](int s, Regs &r) {
     const int kb0 = s * KC;  // first block of the stage
@@ -206,6 +223,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
     for (int j = 0; j < Regs::BLOADS; j++)
       r.b[j] = *reinterpret_cast<const uint4 *>(asrc + boff[j] + (int64_t)kb0 * QK);
     if (dthread) r.d = dsrc[doff + kb0];
+    if (gthread) r.gs = gsrc[s * NG];
   };
 
   auto lstore = [&](int buf, const Regs &r) {
@@ -256,6 +274,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       *reinterpret_cast<uint4 *>(&L.b[buf][q / (2 * KC)][(q % (2 * KC)) * 16]) = r.b[j];
     }
     if (dthread) L.d[buf][tid / KC][tid % KC] = r.d;
+    if (gthread) L.gs[buf][tid / (NG * MF_ROWS)][(tid / MF_ROWS) % NG][tid % MF_ROWS] = r.gs;
   };
 
   float acc[NMAT][16];
@@ -276,8 +295,21 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
         const v4i av = *reinterpret_cast<const v4i *>(arow0 + m * (MF_ROWS * ROWB) + kb * QK);
         const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
+        if constexpr (GS) {
+          // rows wm * 32 + 8 q + 4 grp + (0..3) of the tile: four float4 reads
+          const float *gr = &L.gs[buf][m][kb * QK / 64][wm * 32 + 4 * grp];
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc[m][r] += d * (float)I[r];
+          for (int q = 0; q < 4; q++) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(gr + 8 * q);
+            acc[m][4 * q] = fmaf(d * g4.x, (float)I[4 * q], acc[m][4 * q]);
+            acc[m][4 * q + 1] = fmaf(d * g4.y, (float)I[4 * q + 1], acc[m][4 * q + 1]);
+            acc[m][4 * q + 2] = fmaf(d * g4.z, (float)I[4 * q + 2], acc[m][4 * q + 2]);
+            acc[m][4 * q + 3] = fmaf(d * g4.w, (float)I[4 * q + 3], acc[m][4 * q + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[m][r] += d * (float)I[r];
+        }
       }
     }
   };
@@ -330,15 +362,15 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   int out_row = 0;
   if (valid) out_row = (ti.y < 0) ? P + i : a.perm[ti.y + i];
   const int rbase = r0 + wm * 32;
-  const float *sc = a.scales + (int64_t)ti.x * (2 * a.F + a.H);
+  const float *sc = a.scales + (int64_t)ti.x * a.scale_stride;
   if constexpr (MODE == MF_GATEUP) {
     float h[16];
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int f = rbase + 8 * (r >> 2) + 4 * grp + (r & 3);
-      const float gv = sc[f] * acc[0][r];
-      const float uv = sc[a.F + f] * acc[1][r];
+      const float gv = (GS ? 1.0f : sc[f]) * acc[0][r];
+      const float uv = (GS ? 1.0f : sc[a.F + f]) * acc[1][r];
       h[r] = (gv / (1.0f + expf(-gv))) * uv;
       amax = fmaxf(amax, fabsf(h[r]));
     }
@@ -371,10 +403,10 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       for (int rr = 0; rr < 4; rr++) {
         const int f = rbase + 8 * rr + 4 * grp;
         float4 v;
-        v.x = sd[f] * acc[0][4 * rr];
-        v.y = sd[f + 1] * acc[0][4 * rr + 1];
-        v.z = sd[f + 2] * acc[0][4 * rr + 2];
-        v.w = sd[f + 3] * acc[0][4 * rr + 3];
+        v.x = (GS ? 1.0f : sd[f]) * acc[0][4 * rr];
+        v.y = (GS ? 1.0f : sd[f + 1]) * acc[0][4 * rr + 1];
+        v.z = (GS ? 1.0f : sd[f + 2]) * acc[0][4 * rr + 2];
+        v.w = (GS ? 1.0f : sd[f + 3]) * acc[0][4 * rr + 3];
         *reinterpret_cast<float4 *>(yrow + 8 * rr) = v;
       }
     }
@@ -399,10 +431,16 @@ static hipError_t launch_mf(const FfnArgs &a, const int4 *tiles, const int32_t *
   const int rows = (MODE == MF_GATEUP) ? a.F : a.H;
   const int K = (MODE == MF_GATEUP) ? a.H : a.F;
   if (rows % MF_ROWS || K % (MF_KC * QK) || gmax % 8) return hipErrorInvalidValue;
+  if (a.gs != 0 && a.gs != 64) return hipErrorInvalidValue;
   const int nf = rows / MF_ROWS;
   const int64_t nwork = (int64_t)nf * gmax;
   if (nwork > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles, gmax, nf);
+  if (a.gs)
+    hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC, true>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles,
+                       gmax, nf);
+  else
+    hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC, false>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles,
+                       gmax, nf);
   return hipGetLastError();
 }
 
