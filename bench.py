@@ -58,7 +58,7 @@ def read_traffic(workload: str, T: int):
 class Stack:
     """L stacked layers of one workload, resident on the device."""
 
-    def __init__(self, wl_index: int, layers: int, wbits: int | None = None):
+    def __init__(self, wl_index: int, layers: int, wbits: int | None = None, scale_group: int = 0):
         import numpy as np
         import torch
         import quantized_moe_sigmoid_amd as q
@@ -68,6 +68,9 @@ class Stack:
         self.wl = dict(synth.WORKLOADS[wl_index])
         if wbits is not None:
             self.wl["wbits"] = wbits
+        if scale_group:
+            self.wl["scale_group"] = scale_group
+            self.wl["name"] += f"_gs{scale_group}"
         wl = self.wl
         self.cfg = q.make_cfg(**wl)
         self.blob = q.blob_bytes(self.cfg)
@@ -82,7 +85,8 @@ class Stack:
             synth.device.fill_blobs(blobs, seed, l, 0, ne, self.blob, wl["wbits"])
             inp = synth.layer_inputs(seed, l, tokens=1, hidden=wl["hidden"], ffn=wl["ffn"],
                                      n_experts=wl["n_experts"], has_shared=wl["has_shared"], wbits=wl["wbits"],
-                                     zipf=wl.get("zipf", False), with_blobs=False)
+                                     zipf=wl.get("zipf", False), with_blobs=False,
+                                     scale_group=wl.get("scale_group", 0))
             up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
             w = q.Weights(blobs, up(inp["scales"]), up(inp["router_w"]), up(inp["router_bias"]))
             self.layers.append((seed, w))
@@ -118,6 +122,12 @@ class Stack:
         return us
 
 
+def _row_scale_bytes(wl, n_inputs: int) -> int:
+    """fp32 scale bytes of one weight row of n_inputs: one per row, or one per group."""
+    g = wl.get("scale_group", 0)
+    return 4 if g == 0 else 4 * (n_inputs // g)
+
+
 def gateup_bytes(wl, U: int, T: int) -> int:
     """Algorithmic HBM bytes of one gate/up launch: the packed gate and up rows plus their
     fp32 scales of the U routed (+ shared) experts, the Q8_0 activations read once, and
@@ -125,7 +135,7 @@ def gateup_bytes(wl, U: int, T: int) -> int:
     H, F, k, wb = wl["hidden"], wl["ffn"], wl["top_k"], wl["wbits"]
     S = 1 if wl["has_shared"] else 0
     nexp = U + S
-    weights = nexp * 2 * F * (H * wb // 8 + 4)
+    weights = nexp * 2 * F * (H * wb // 8 + _row_scale_bytes(wl, H))
     acts = T * (H + 8 * (H // 32))
     rows_out = T * k + S * T
     hout = rows_out * (F + 8 * (F // 32))
@@ -136,7 +146,7 @@ def layer_weight_bytes(wl, U: int) -> int:
     """Packed weights + per-row scales of the experts one layer call streams."""
     H, F, wb = wl["hidden"], wl["ffn"], wl["wbits"]
     nexp = U + (1 if wl["has_shared"] else 0)
-    return nexp * (2 * F * (H * wb // 8) + H * (F * wb // 8) + 4 * (2 * F + H))
+    return nexp * (2 * F * (H * wb // 8 + _row_scale_bytes(wl, H)) + H * (F * wb // 8 + _row_scale_bytes(wl, F)))
 
 
 def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
@@ -240,7 +250,8 @@ def cpu_baseline(stack, T: int, budget_s: float):
     seed, _ = stack.layers[0]
     T = min(T, 64)
     inp = synth.layer_inputs(seed, 0, tokens=T, hidden=wl["hidden"], ffn=wl["ffn"], n_experts=wl["n_experts"],
-                             has_shared=wl["has_shared"], wbits=wl["wbits"], zipf=wl.get("zipf", False))
+                             has_shared=wl["has_shared"], wbits=wl["wbits"], zipf=wl.get("zipf", False),
+                             scale_group=wl.get("scale_group", 0))
     cfg = oracle.make_cfg(**wl)
     calls = 0
     t0 = time.perf_counter()
@@ -330,6 +341,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--wbits", type=int, default=None)
+    ap.add_argument("--scale-group", type=int, default=0, choices=[0, 64],
+                    help="64: group-scaled weights, one fp32 scale per 64 inputs of a row")
     ap.add_argument("--tokens", type=str, default=None, help="comma list of T; the last is the headline")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-graph", action="store_true")
@@ -363,7 +376,7 @@ def main():
         log(f"copy kernel ({args.calib_mb} MiB): {copy_gbs:.0f} GB/s read+write")
     wl0 = synth.WORKLOADS[args.config]
     Ts = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl0["tokens"])
-    stack = Stack(args.config, args.layers, args.wbits)
+    stack = Stack(args.config, args.layers, args.wbits, args.scale_group)
     wl = stack.wl
     results = []
     for T in Ts:
@@ -421,7 +434,8 @@ def main():
         "data": "synthetic (seeded SplitMix64; random int weights, N(0,1) activations)",
         "config": {"workload": wl["name"], "hidden": wl["hidden"], "ffn": wl["ffn"], "n_experts": wl["n_experts"],
                    "top_k": wl["top_k"], "n_group": wl["n_group"], "topk_group": wl["topk_group"],
-                   "has_shared": wl["has_shared"], "wbits": wl["wbits"], "tokens": T,
+                   "has_shared": wl["has_shared"], "wbits": wl["wbits"],
+                   "scale_group": wl.get("scale_group", 0), "tokens": T,
                    "stacked_layers": stack.L, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -546,9 +546,10 @@ struct FastCtx {
   const float *xds;  // LDS block scales [ntmax][nkb]
   float *obuf;       // LDS results [NMAT][8][TILE]
   int r0;            // first row of the tile
+  const float *gs0, *gs1;  // group scales [rows][K/64] of the two matrices (GS only)
 };
 
-template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC>
+template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS>
 __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, int wv) {
   constexpr int RPI = WAVE / LPR;
   constexpr int CW = Fmt<WB>::CHUNK / 4;
@@ -569,11 +570,13 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
 
   for (int b0 = 0; b0 < WR; b0 += RPB) {
     int64_t roff[BR];
+    int64_t goff[BR];  // group-scale offset of the row (GS)
 #pragma unroll
     for (int j = 0; j < BR; j++) {
       int rw = b0 + j * RPI + rs;
       rw = rw < WR ? rw : WR - 1;
       roff[j] = (int64_t)(c.r0 + wv * WR + rw) * c.rb;
+      goff[j] = (int64_t)(c.r0 + wv * WR + rw) * (c.K / 64);
     }
     float acc[V];
 #pragma unroll
@@ -587,6 +590,13 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
           load_chunk<WB>((m == 0 ? c.mat0 : c.mat1) + roff[j] + (int64_t)ch * Fmt<WB>::CHUNK, w[j][m]);
+      float gsr[BR][NMAT];  // the chunk's group scale per row (a chunk lies in one group)
+      if constexpr (GS) {
+#pragma unroll
+        for (int j = 0; j < BR; j++)
+#pragma unroll
+          for (int m = 0; m < NMAT; m++) gsr[j][m] = (m == 0 ? c.gs0 : c.gs1)[goff[j] + ch * BPC * QK / 64];
+      }
       Act<WB> act[NTC];
 #pragma unroll
       for (int t = 0; t < NTC; t++)
@@ -598,8 +608,14 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
           int u[Unp<WB>::N];
           unpack_chunk<WB>(w[j][m], u);
 #pragma unroll
-          for (int t = 0; t < NTC; t++)
-            if (t < nt) acc[(j * NMAT + m) * NTC + t] += dot_unpacked<WB>(u, act[t]);
+          for (int t = 0; t < NTC; t++) {
+            if (t < nt) {
+              if constexpr (GS)
+                acc[(j * NMAT + m) * NTC + t] = fmaf(gsr[j][m], dot_unpacked<WB>(u, act[t]), acc[(j * NMAT + m) * NTC + t]);
+              else
+                acc[(j * NMAT + m) * NTC + t] += dot_unpacked<WB>(u, act[t]);
+            }
+          }
         }
     }
     int base = 0;
@@ -616,7 +632,8 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
   }
 }
 
-template <int WB, int LPR, int CPL, int MODE, int WR>
+// GS: one scale per 64 inputs of a row, applied per chunk (see gemv_kernel).
+template <int WB, int LPR, int CPL, int MODE, int WR, bool GS = false>
 __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int TILE = 4 * WR;
@@ -648,6 +665,11 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   c.xds = xds;
   c.obuf = obuf;
   c.r0 = blockIdx.x * TILE;
+  {
+    const int64_t ngh = (int64_t)a.F * (a.H / 64);
+    c.gs0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * ngh;
+    c.gs1 = sc + ngh;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int8_t *asrc = (MODE == MODE_GATEUP) ? a.xq : a.hq;
@@ -678,17 +700,17 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
     }
     __syncthreads();
     if (nt <= 1)
-      fast_pass<WB, NMAT, LPR, CPL, WR, 1>(c, nt, lane, wv);
+      fast_pass<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
     else
-      fast_pass<WB, NMAT, LPR, CPL, WR, 2>(c, nt, lane, wv);
+      fast_pass<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
     __syncthreads();
     // epilogue over the tile's rows x nt tokens
     if constexpr (MODE == MODE_GATEUP) {
       const float *sg = sc, *su = sc + a.F;
       for (int p = tid; p < nt * TILE; p += 256) {  // one Q8_0 block of h per 32 consecutive lanes
         const int t = p / TILE, i = p % TILE, r = c.r0 + i;
-        const float g = (sg[r] * Fmt<WB>::INV) * obuf[(0 * 8 + t) * TILE + i];
-        const float u = (su[r] * Fmt<WB>::INV) * obuf[(1 * 8 + t) * TILE + i];
+        const float g = ((GS ? 1.0f : sg[r]) * Fmt<WB>::INV) * obuf[(0 * 8 + t) * TILE + i];
+        const float u = ((GS ? 1.0f : su[r]) * Fmt<WB>::INV) * obuf[(1 * 8 + t) * TILE + i];
         const float v = (g / (1.0f + expf(-g))) * u;
         float am = fabsf(v);
         am = max32(am);
@@ -703,7 +725,7 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
       const float *sd = sc + 2 * a.F;
       for (int p = tid; p < nt * TILE; p += 256) {
         const int t = p / TILE, i = p % TILE, r = c.r0 + i;
-        a.ypair[(int64_t)orow[t] * a.H + r] = (sd[r] * Fmt<WB>::INV) * obuf[t * TILE + i];
+        a.ypair[(int64_t)orow[t] * a.H + r] = ((GS ? 1.0f : sd[r]) * Fmt<WB>::INV) * obuf[t * TILE + i];
       }
     }
     __syncthreads();
@@ -897,7 +919,10 @@ __device__ __forceinline__ void pipe_list_pairs(const PipeLds &L, int e, int P, 
   if (lane == 0) *nout = cnt;
 }
 
-template <int WB, int LPR, int MODE, int WR>
+// GS: one scale per 64 inputs of a row; the lane's chunk lies in one group, whose
+// scale per tile row is loaded with the row's weights and multiplies the chunk's
+// products (the row scales of the epilogue are then 1).
+template <int WB, int LPR, int MODE, int WR, bool GS = false>
 __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int RPI = WAVE / LPR;
@@ -933,12 +958,16 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
   const uint32_t lane_w = (uint32_t)(rs * rb + sub * Fmt<WB>::CHUNK);
   const uint32_t lane_x = (uint32_t)(sub * BPC * QK);
   uint32_t w[R][NMAT][CW];
+  float gsr[R][NMAT];  // group scales of the lane's chunk per tile row (GS)
   // weights of expert e (a.E: the shared expert), tile rows r0..: rows
   // h * RH .. h * RH + RH - 1 of the lane's tile rows (h < 0: all rows), preceded
   // by the row scales when h <= 0 (raw: 1/S is applied at use, so nothing waits
   // for these loads before the epilogue)
   auto issue = [&](int e, int r0, int h, float &t0, float &t1) {
-    if (h <= 0 && pt < 2) {
+    if (GS) {
+      t0 = 1.0f;
+      t1 = 1.0f;
+    } else if (h <= 0 && pt < 2) {
       const float *sc = a.scales + (int64_t)e * a.scale_stride;
       if constexpr (MODE == MODE_GATEUP) {
         t0 = sc[r0 + pi];
@@ -958,6 +987,18 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
       const int64_t roff = (int64_t)(r0 + wvu * WR + j * RPI) * rb;
 #pragma unroll
       for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff + lane_w, w[j][m]);
+    }
+    if constexpr (GS) {
+      // group scales: gate [F][H/64] | up [F][H/64] | down [H][F/64]
+      const int64_t ngh = (int64_t)a.F * (a.H / 64);
+      const float *gsc = a.scales + (int64_t)e * a.scale_stride + ((MODE == MODE_GATEUP) ? 0 : 2 * ngh);
+#pragma unroll
+      for (int j = 0; j < R; j++) {
+        if (h >= 0 && j / RH != h) continue;
+        const int64_t goff = (int64_t)(r0 + wvu * WR + j * RPI + rs) * (K / 64) + lane_x / 64;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) gsr[j][m] = gsc[m * ngh + goff];
+      }
     }
   };
 
@@ -1079,7 +1120,12 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
               int uq[Unp<WB>::N];
               unpack_chunk<WB>(w[j][m], uq);
 #pragma unroll
-              for (int t = 0; t < NTC; t++) acc[(jj * NMAT + m) * NTC + t] += dot_unpacked<WB>(uq, act[t]);
+              for (int t = 0; t < NTC; t++) {
+                if constexpr (GS)
+                  acc[(jj * NMAT + m) * NTC + t] = fmaf(gsr[j][m], dot_unpacked<WB>(uq, act[t]), acc[(jj * NMAT + m) * NTC + t]);
+                else
+                  acc[(jj * NMAT + m) * NTC + t] += dot_unpacked<WB>(uq, act[t]);
+              }
             }
           if (last && en >= 0) {
             // ordered after the products: hoisted above them the loads would need
@@ -1155,13 +1201,13 @@ static int resident_groups(Kern k, int threads) {
   return g;
 }
 
-template <int WB, int LPR, int MODE>
+template <int WB, int LPR, int MODE, bool GS>
 static hipError_t launch_pipe(const FfnArgs &a, int nrows, hipStream_t s) {
   constexpr int WRMAX = 64 * (WAVE / LPR) / (Fmt<WB>::CHUNK / 4);
   constexpr int WR = (MODE == MODE_DOWN) ? (WRMAX < 16 ? WRMAX : 16) : 8;
   constexpr int TILE = 4 * WR;
   if (nrows % TILE) return hipErrorNotSupported;
-  auto kern = gemv_pipe_kernel<WB, LPR, MODE, WR>;
+  auto kern = gemv_pipe_kernel<WB, LPR, MODE, WR, GS>;
   const int res = resident_groups(kern, 256);
   if (res <= 0) return hipErrorNotSupported;
   const int64_t units = (int64_t)(a.has_shared + min(a.E, a.T * a.k)) * (nrows / TILE);
@@ -1197,7 +1243,7 @@ static int pick_lpr(int nchunk) {
   return l;
 }
 
-template <int WB, int LPR, int CPL, int MODE>
+template <int WB, int LPR, int CPL, int MODE, bool GS>
 static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int K, hipStream_t s) {
   constexpr int WR = (MODE == MODE_DOWN && LPR < 64) ? 16 : 8;
   constexpr int TILE = 4 * WR;
@@ -1210,11 +1256,11 @@ static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int 
   const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(float) + (size_t)NMAT * 8 * TILE * sizeof(float) +
                      16 * sizeof(int);
   dim3 grid(nrows / TILE, slots_grid.y);
-  hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR>), grid, dim3(256), lds, s, a, ntmax);
+  hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR, GS>), grid, dim3(256), lds, s, a, ntmax);
   return hipGetLastError();
 }
 
-template <int WB, int MODE>
+template <int WB, int MODE, bool GS>
 static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
   const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;
@@ -1223,34 +1269,15 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   const int lpr = pick_lpr(nchunk);
   const int cpl = nchunk / lpr;
   const int slots = a.has_shared + min(a.E, a.T * a.k);
-  if (a.gs != 0) {  // group scales: the generic kernel
-    dim3 grid(NROWS / GEMV_ROWS, slots);
-    const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(float) +
-                       (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
-    if (a.gs != 64 || K % 64) return hipErrorInvalidValue;
-    switch (lpr) {
-#define COLI_LPR_CASE(L) \
-  case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE, true>), grid, dim3(256), lds, s, a); break;
-      COLI_LPR_CASE(64)
-      COLI_LPR_CASE(32)
-      COLI_LPR_CASE(16)
-      COLI_LPR_CASE(8)
-      COLI_LPR_CASE(4)
-      COLI_LPR_CASE(2)
-      COLI_LPR_CASE(1)
-#undef COLI_LPR_CASE
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
   // one chunk per lane and row, and the tile fits in registers: weights stay resident
   constexpr int NMATC = (MODE == MODE_GATEUP) ? 2 : 1;
   if constexpr (WB != 2 && (Fmt<WB>::CHUNK / 4) * NMATC * 8 <= 64) {
     if (cpl == 1 && (lpr == 64 || lpr == 32)) {
       hipError_t r = hipErrorNotSupported;
       if (a.idx != nullptr)
-        r = (lpr == 64) ? launch_pipe<WB, 64, MODE>(a, NROWS, s) : launch_pipe<WB, 32, MODE>(a, NROWS, s);
-      if (r == hipErrorNotSupported)
+        r = (lpr == 64) ? launch_pipe<WB, 64, MODE, GS>(a, NROWS, s) : launch_pipe<WB, 32, MODE, GS>(a, NROWS, s);
+      // the register-resident kernel keeps one scale per row
+      if (r == hipErrorNotSupported && !GS)
         r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
       if (r != hipErrorNotSupported) return r;
     }
@@ -1259,11 +1286,11 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   if (lpr == 64 || lpr == 32) {
     hipError_t r = hipErrorNotSupported;
     const dim3 sg(1, slots);
-    if (lpr == 64 && cpl == 1) r = launch_fast<WB, 64, 1, MODE>(a, sg, NROWS, K, s);
-    else if (lpr == 64 && cpl == 2) r = launch_fast<WB, 64, 2, MODE>(a, sg, NROWS, K, s);
-    else if (lpr == 64 && cpl == 3) r = launch_fast<WB, 64, 3, MODE>(a, sg, NROWS, K, s);
-    else if (lpr == 32 && cpl == 1) r = launch_fast<WB, 32, 1, MODE>(a, sg, NROWS, K, s);
-    else if (lpr == 32 && cpl == 3) r = launch_fast<WB, 32, 3, MODE>(a, sg, NROWS, K, s);
+    if (lpr == 64 && cpl == 1) r = launch_fast<WB, 64, 1, MODE, GS>(a, sg, NROWS, K, s);
+    else if (lpr == 64 && cpl == 2) r = launch_fast<WB, 64, 2, MODE, GS>(a, sg, NROWS, K, s);
+    else if (lpr == 64 && cpl == 3) r = launch_fast<WB, 64, 3, MODE, GS>(a, sg, NROWS, K, s);
+    else if (lpr == 32 && cpl == 1) r = launch_fast<WB, 32, 1, MODE, GS>(a, sg, NROWS, K, s);
+    else if (lpr == 32 && cpl == 3) r = launch_fast<WB, 32, 3, MODE, GS>(a, sg, NROWS, K, s);
     if (r != hipErrorNotSupported) return r;
   }
   dim3 grid(NROWS / GEMV_ROWS, slots);
@@ -1271,7 +1298,7 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
                      (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
   switch (lpr) {
 #define COLI_LPR_CASE(L) \
-  case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE>), grid, dim3(256), lds, s, a); break;
+  case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE, GS>), grid, dim3(256), lds, s, a); break;
     COLI_LPR_CASE(64)
     COLI_LPR_CASE(32)
     COLI_LPR_CASE(16)
@@ -1285,23 +1312,21 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s) {
+template <int MODE>
+static hipError_t launch_fmt(int wfmt, const FfnArgs &a, hipStream_t s) {
+  if (a.gs != 0 && a.gs != 64) return hipErrorInvalidValue;
+  const bool gs = a.gs != 0;
   switch (wfmt) {
-    case 4: return launch_mode<4, MODE_GATEUP>(a, s);
-    case 8: return launch_mode<8, MODE_GATEUP>(a, s);
-    case 2: return launch_mode<2, MODE_GATEUP>(a, s);
+    case 4: return gs ? launch_mode<4, MODE, true>(a, s) : launch_mode<4, MODE, false>(a, s);
+    case 8: return gs ? launch_mode<8, MODE, true>(a, s) : launch_mode<8, MODE, false>(a, s);
+    case 2: return gs ? launch_mode<2, MODE, true>(a, s) : launch_mode<2, MODE, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s) {
-  switch (wfmt) {
-    case 4: return launch_mode<4, MODE_DOWN>(a, s);
-    case 8: return launch_mode<8, MODE_DOWN>(a, s);
-    case 2: return launch_mode<2, MODE_DOWN>(a, s);
-  }
-  return hipErrorInvalidValue;
-}
+hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s) { return launch_fmt<MODE_GATEUP>(wfmt, a, s); }
+
+hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s) { return launch_fmt<MODE_DOWN>(wfmt, a, s); }
 
 // out[t] = sum_j w[t][j] * ypair[t*k + j] (j ascending) + ypair[P + t] (shared).
 // The slots are loaded eight at a time (independent loads in flight together) and
