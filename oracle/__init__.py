@@ -31,12 +31,13 @@ class Cfg(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32),
                 ("top_k", C.c_int32), ("n_group", C.c_int32), ("topk_group", C.c_int32),
                 ("rsf", C.c_float), ("has_shared", C.c_int32), ("wbits", C.c_int32),
-                ("scale_group", C.c_int32)]
+                ("scale_group", C.c_int32), ("topp", C.c_float)]
 
 
 def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, has_shared=False, wbits=4,
-             scale_group=0, **_ignored) -> Cfg:
-    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group)
+             scale_group=0, topp=0.0, **_ignored) -> Cfg:
+    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group,
+               topp)
 
 
 _lib = None
@@ -144,7 +145,7 @@ def group(cfg: Cfg, idx):
     nact = np.zeros(1, np.int32)
     _check(lib().coli_ref_moe_group(C.byref(cfg), _p(idx), T, _p(cnt), _p(off), _p(perm), _p(active),
                                     _p(nact)), "group")
-    return cnt, off, perm, active[: nact[0]].copy()
+    return cnt, off, perm[: off[E]].copy(), active[: nact[0]].copy()
 
 
 def expert_ffn(hidden, ffn, wbits, blob, scales, xq, xd, scale_group=0):

@@ -169,6 +169,7 @@ static int cfg_ok(const coli_ref_cfg *c) {
   if (c->has_shared != 0 && c->has_shared != 1) return 0;
   if (c->scale_group != 0 && c->scale_group != 64) return 0;
   if (c->scale_group && (c->hidden % c->scale_group || c->ffn % c->scale_group)) return 0;
+  if (!(c->topp >= 0.0f && c->topp <= 1.0f)) return 0;
   return 1;
 }
 
@@ -215,7 +216,29 @@ static void route_token(const coli_ref_cfg *cfg, const float *W, const float *bi
   }
   double S = 0.0;
   for (int j = 0; j < cfg->top_k; j++) S += s[idx[j]];
-  for (int j = 0; j < cfg->top_k; j++) w[j] = (float)((s[idx[j]] / S) * (double)cfg->rsf);
+  int kept = cfg->top_k;
+  if (cfg->topp > 0.0f) {
+    /* adaptive top-p: the shortest prefix of the slots (descending c) whose summed
+     * scores reach topp * S; its sum, in the same order, renormalises the weights */
+    const double target = (double)cfg->topp * S;
+    double cum = 0.0;
+    for (int j = 0; j < cfg->top_k; j++) {
+      cum += s[idx[j]];
+      if (cum >= target) {
+        kept = j + 1;
+        break;
+      }
+    }
+    S = cum;
+  }
+  for (int j = 0; j < cfg->top_k; j++) {
+    if (j < kept) {
+      w[j] = (float)((s[idx[j]] / S) * (double)cfg->rsf);
+    } else {
+      idx[j] = -1;
+      w[j] = 0.0f;
+    }
+  }
 }
 
 int coli_ref_moe_route_scores(const coli_ref_cfg *cfg, const float *router_w, const float *router_bias,
@@ -264,16 +287,19 @@ int coli_ref_moe_group(const coli_ref_cfg *cfg, const int32_t *topk_idx, int32_t
   const int E = cfg->n_experts;
   const int64_t P = (int64_t)T * cfg->top_k;
   if (P > 0 && (!topk_idx || !pair_perm)) return -1;
+  /* index -1 is an empty slot (adaptive top-p): part of no expert */
   for (int64_t p = 0; p < P; p++)
-    if (topk_idx[p] < 0 || topk_idx[p] >= E) return -2;
+    if (topk_idx[p] < -1 || topk_idx[p] >= E) return -2;
   for (int e = 0; e < E; e++) expert_cnt[e] = 0;
-  for (int64_t p = 0; p < P; p++) expert_cnt[topk_idx[p]]++;
+  for (int64_t p = 0; p < P; p++)
+    if (topk_idx[p] >= 0) expert_cnt[topk_idx[p]]++;
   expert_off[0] = 0;
   for (int e = 0; e < E; e++) expert_off[e + 1] = expert_off[e] + expert_cnt[e];
   int32_t *fill = malloc(sizeof(int32_t) * (size_t)E);
   if (!fill) return -3;
   for (int e = 0; e < E; e++) fill[e] = expert_off[e];
-  for (int64_t p = 0; p < P; p++) pair_perm[fill[topk_idx[p]]++] = (int32_t)p;
+  for (int64_t p = 0; p < P; p++)
+    if (topk_idx[p] >= 0) pair_perm[fill[topk_idx[p]]++] = (int32_t)p;
   free(fill);
   int32_t u = 0;
   for (int e = 0; e < E; e++)
@@ -380,7 +406,7 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
   const int32_t gs = cfg->scale_group;
   const int64_t srow = gs ? 3 * (int64_t)F * (H / gs) : 2 * (int64_t)F + H;  /* scales per expert */
   for (int64_t p = 0; p < (int64_t)T * k; p++)
-    if (topk_idx[p] < 0 || topk_idx[p] >= E) return -2;
+    if (topk_idx[p] < -1 || topk_idx[p] >= E) return -2;  /* -1: empty slot (adaptive top-p) */
   const int nslot = k + (cfg->has_shared ? 1 : 0);
   int bad = 0;
 #pragma omp parallel
@@ -397,12 +423,14 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
         coli_ref_quantize_q8_0(x + (int64_t)t * H, 1, H, xq, xd);
         for (int j = 0; j < nslot; j++) {
           int64_t e = j < k ? topk_idx[(int64_t)t * k + j] : E; /* shared expert stored after the routed ones */
+          if (e < 0) continue;                                  /* empty slot: weight 0, never read */
           coli_ref_expert_ffn(H, F, cfg->wbits, gs, experts + e * blob, scales + e * srow, xq, xd, NULL, NULL,
                               NULL, NULL, NULL, y + (int64_t)j * H);
         }
         for (int32_t r = 0; r < H; r++) {
           double acc = 0.0;
-          for (int j = 0; j < k; j++) acc += (double)topk_w[(int64_t)t * k + j] * y[(int64_t)j * H + r];
+          for (int j = 0; j < k; j++)
+            if (topk_idx[(int64_t)t * k + j] >= 0) acc += (double)topk_w[(int64_t)t * k + j] * y[(int64_t)j * H + r];
           if (cfg->has_shared) acc += y[(int64_t)k * H + r];
           out[(int64_t)t * H + r] = (float)acc;
         }

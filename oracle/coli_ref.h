@@ -48,6 +48,7 @@ typedef struct {
   int32_t has_shared;   /* 0/1: shared expert stored after the routed ones */
   int32_t wbits;        /* 2, 4 or 8 */
   int32_t scale_group;  /* 0: one fp32 scale per row; 64: one per 64 consecutive inputs of a row */
+  float   topp;         /* 0: plain top-k; 0 < topp <= 1: adaptive expert top-p (see coli_ref_moe_route) */
 } coli_ref_cfg;
 
 /* Q8_0 of rows x cols fp32 values (cols % 32 == 0): q int8 [rows, cols], d fp32 [rows, cols/32]. */
@@ -60,7 +61,11 @@ int coli_ref_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q
 int coli_ref_pack(int32_t wbits, const int8_t *q, int64_t n, uint8_t *out);
 int coli_ref_unpack(int32_t wbits, const uint8_t *in, int64_t n, int8_t *q);
 
-/* Router for T tokens: topk_idx int32 [T, k], topk_w fp32 [T, k]. */
+/* Router for T tokens: topk_idx int32 [T, k], topk_w fp32 [T, k]. With topp > 0 (adaptive
+ * expert top-p, JustVugg/colibri README, "Useful knobs", --topp) only the shortest prefix of the
+ * k slots whose summed scores reach topp of the k slots' sum is kept (at least one slot); the
+ * kept weights are renormalised over the kept slots and the dropped slots hold index -1 and
+ * weight 0. The grouping and the FFN skip index -1. */
 int coli_ref_moe_route(const coli_ref_cfg *cfg, const float *router_w, const float *router_bias,
                        const float *x, int32_t T, int32_t *topk_idx, float *topk_w);
 

@@ -189,3 +189,22 @@ def test_layer_group_scales_rejects_bad_group(oracle_lib):
         cfg = oracle_lib.make_cfg(hidden=H, ffn=64, n_experts=2, top_k=1, wbits=4, scale_group=gs)
         with pytest.raises(ValueError):
             oracle_lib.layer(cfg, inp["blobs"], inp["scales"], inp["router_w"], inp["router_bias"], inp["x"])
+
+
+def test_layer_topp_is_sum_over_kept_slots(oracle_lib):
+    """With adaptive top-p the layer is the weighted sum over the kept slots only (plus the
+    shared expert), each evaluated by the single-expert oracle."""
+    H, F, E, k = 128, 64, 8, 4
+    inp = synth.layer_inputs(81, 0, tokens=6, hidden=H, ffn=F, n_experts=E, has_shared=True, wbits=4)
+    cfg = oracle_lib.make_cfg(hidden=H, ffn=F, n_experts=E, top_k=k, rsf=2.0, has_shared=True, wbits=4, topp=0.6)
+    out, idx, w = oracle_lib.layer(cfg, inp["blobs"], inp["scales"], inp["router_w"], inp["router_bias"], inp["x"])
+    assert np.any(idx == -1)
+    xq, xd = oracle_lib.quantize_q8_0(inp["x"])
+    for t in range(6):
+        acc = np.zeros(H)
+        for j in range(k):
+            if idx[t, j] >= 0:
+                acc += float(w[t, j]) * oracle_lib.expert_ffn(H, F, 4, inp["blobs"][idx[t, j]], inp["scales"][idx[t, j]],
+                                                              xq[t], xd[t])["y"]
+        acc += oracle_lib.expert_ffn(H, F, 4, inp["blobs"][E], inp["scales"][E], xq[t], xd[t])["y"]
+        assert np.array_equal(out[t], acc.astype(np.float32))

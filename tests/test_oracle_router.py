@@ -137,3 +137,70 @@ def test_group_invariants(oracle_lib, E, k, T):
         seg = perm[off[e]:off[e + 1]]
         assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
     assert np.array_equal(active, np.nonzero(cnt)[0])
+
+
+# ---------------------------------------------------------------- adaptive expert top-p
+def _topp_inputs(seed, T, E, H):
+    x = synth.activations(seed, 0, T, H)
+    W = synth.router_weight(seed, 0, E, H, std=0.05)
+    b = synth.router_bias(seed, 0, E)
+    return x, W, b
+
+
+@pytest.mark.parametrize("E,G,Gk,k,p", [(16, 1, 1, 4, 0.7), (64, 1, 1, 8, 0.5), (32, 4, 2, 6, 0.75),
+                                        (256, 8, 4, 8, 0.7), (8, 8, 3, 3, 0.3)])
+def test_router_topp_bruteforce(oracle_lib, E, G, Gk, k, p):
+    """The kept slots are the shortest prefix of the plain route (descending c) whose
+    scores sum to at least p of the k slots' sum, recomputed here from the plain route
+    and its scores; kept weights renormalised over the kept slots, dropped slots -1 / 0."""
+    T, H, rsf = 24, 64, 2.5
+    x, W, b = _topp_inputs(300 + E + k, T, E, H)
+    plain = oracle_lib.make_cfg(hidden=H, ffn=32, n_experts=E, top_k=k, n_group=G, topk_group=Gk, rsf=rsf)
+    idx0, w0, s = oracle_lib.route(plain, W, b, x, scores=True)
+    cfg = oracle_lib.make_cfg(hidden=H, ffn=32, n_experts=E, top_k=k, n_group=G, topk_group=Gk, rsf=rsf, topp=p)
+    idx, w = oracle_lib.route(cfg, W, b, x)
+    dropped_any = False
+    for t in range(T):
+        st = s[t, idx0[t]]                      # scores of the plain slots, slot order
+        cum = np.cumsum(st)                     # sequential float64 sums
+        m = int(np.argmax(cum >= np.float64(np.float32(p)) * cum[-1])) + 1
+        assert 1 <= m <= k
+        assert np.array_equal(idx[t, :m], idx0[t, :m]) and np.all(idx[t, m:] == -1)
+        want = ((st[:m] / cum[m - 1]) * np.float64(np.float32(rsf))).astype(np.float32)
+        assert np.array_equal(w[t, :m], want) and np.all(w[t, m:] == 0.0)
+        # kept share reaches p; without the last kept slot it does not
+        assert cum[m - 1] >= p * cum[-1] * (1 - 1e-12)
+        if m > 1:
+            assert cum[m - 2] < np.float64(np.float32(p)) * cum[-1]
+        assert abs(float(w[t, :m].astype(np.float64).sum()) - rsf) <= 4 * m * np.spacing(np.float32(rsf))
+        dropped_any |= m < k
+    assert dropped_any
+
+
+def test_router_topp_one_and_zero_are_plain(oracle_lib):
+    """topp = 0 (off) gives the plain route; topp = 1 keeps every slot."""
+    T, E, H, k = 16, 32, 64, 6
+    x, W, b = _topp_inputs(321, T, E, H)
+    base = dict(hidden=H, ffn=32, n_experts=E, top_k=k, n_group=4, topk_group=2, rsf=1.5)
+    idx0, w0 = oracle_lib.route(oracle_lib.make_cfg(**base), W, b, x)
+    for p in (0.0, 1.0):
+        idx, w = oracle_lib.route(oracle_lib.make_cfg(**base, topp=p), W, b, x)
+        assert np.array_equal(idx, idx0) and np.array_equal(w, w0)
+
+
+def test_group_skips_empty_slots(oracle_lib):
+    """Index -1 (a dropped top-p slot) belongs to no expert; the grouping of the other
+    pairs is the stable sort of their ids by expert."""
+    E, k, T = 16, 4, 50
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    keep = rng.integers(1, k + 1, size=T)
+    for t in range(T):
+        idx[t, keep[t]:] = -1
+    cnt, off, perm, active = oracle_lib.group(_cfg(oracle_lib, E, 1, 1, k, 1.0), idx)
+    flat = idx.ravel()
+    valid = np.nonzero(flat >= 0)[0]
+    assert off[-1] == valid.size == cnt.sum()
+    assert np.array_equal(cnt, np.bincount(flat[valid], minlength=E))
+    assert np.array_equal(perm, valid[np.argsort(flat[valid], kind="stable")])
+    assert np.array_equal(active, np.nonzero(cnt)[0])
