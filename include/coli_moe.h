@@ -87,7 +87,7 @@ typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8 } coli_wfmt;
 /* Layer shape. Limits: hidden and ffn multiples of 128; 1 <= n_experts <= 1024;
  * n_experts % n_group == 0; 1 <= topk_group <= n_group <= 64;
  * 1 <= top_k <= min(64, topk_group * n_experts / n_group); has_shared 0 or 1;
- * wfmt 2, 4 or 8; scale_group 0 or 64. */
+ * wfmt 2, 4 or 8; scale_group 0 or 64; 0 <= topp <= 1. */
 typedef struct {
   int32_t hidden;               /* H */
   int32_t ffn;                  /* F, width of every expert (shared included) */
@@ -99,6 +99,7 @@ typedef struct {
   int32_t has_shared;           /* 1: blob E is a shared expert applied to every token */
   int32_t wfmt;                 /* coli_wfmt, one format for all experts of the layer */
   int32_t scale_group;          /* 0: one scale per weight row; 64: one per 64 inputs of a row */
+  float topp;                   /* 0: plain top-k; 0 < topp <= 1: adaptive expert top-p (see the router) */
 } coli_moe_cfg;
 
 /* Device weights of one layer. experts: 16-byte aligned; router_w: 16-byte aligned;
@@ -129,7 +130,12 @@ int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q
 
 /* Sigmoid noaux_tc router for T tokens: topk_idx int32 [T][k] (expert ids, slot
  * order), topk_w fp32 [T][k]. Uses the workspace for fp64 logits.
- * Follows colibri-strix README, "What's implemented", router item. */
+ * Follows colibri-strix README, "What's implemented", router item.
+ * With cfg->topp > 0 (adaptive expert top-p, JustVugg/colibri README, "Useful knobs",
+ * --topp; opt-in, it changes the router's result): only the shortest prefix of the k
+ * slots whose scores s sum (fp64, slot order) to at least topp times the k slots' sum
+ * is kept, at least one slot; the kept weights are s_j / (that prefix sum) * rsf, and
+ * every dropped slot holds index -1 and weight 0. */
 int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
                    int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream);
 
@@ -139,8 +145,9 @@ int coli_moe_route(const coli_moe_cfg *cfg, const coli_moe_weights *w, const flo
  *   pair_perm int32 [T*k]: pair ids sorted by (expert, p) ascending;
  *   active int32 [E]: experts with cnt > 0, ascending, in the first *n_active entries;
  *   n_active int32 [1].
- * topk_idx values must lie in [0, E) (checked by the kernel: out-of-range ids are
- * counted nowhere and leave n_active = -1).
+ * topk_idx values must lie in [0, E) or be -1, an empty slot (adaptive top-p) that
+ * belongs to no expert; other values are counted nowhere and leave n_active = -1
+ * (checked by the kernel). expert_off[E] is then the number of non-empty pairs.
  * Follows colibri-strix README, "What's implemented", batch-union item. */
 int coli_moe_group(const coli_moe_cfg *cfg, const int32_t *topk_idx, int32_t T, int32_t *expert_cnt,
                    int32_t *expert_off, int32_t *pair_perm, int32_t *active, int32_t *n_active,

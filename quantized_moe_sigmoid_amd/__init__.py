@@ -32,7 +32,7 @@ class Cfg(C.Structure):
     """coli_moe_cfg."""
     _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("n_group", C.c_int32), ("topk_group", C.c_int32), ("routed_scaling_factor", C.c_float),
-                ("has_shared", C.c_int32), ("wfmt", C.c_int32), ("scale_group", C.c_int32)]
+                ("has_shared", C.c_int32), ("wfmt", C.c_int32), ("scale_group", C.c_int32), ("topp", C.c_float)]
 
 
 class _Weights(C.Structure):
@@ -41,8 +41,9 @@ class _Weights(C.Structure):
 
 
 def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, has_shared=False, wbits=4,
-             scale_group=0, **_ignored) -> Cfg:
-    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group)
+             scale_group=0, topp=0.0, **_ignored) -> Cfg:
+    return Cfg(hidden, ffn, n_experts, top_k, n_group, topk_group, rsf, int(bool(has_shared)), wbits, scale_group,
+               topp)
 
 
 @dataclass

@@ -51,6 +51,7 @@ static int check_cfg(const coli_moe_cfg *c) {
   if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return COLI_E_INVALID;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return COLI_E_INVALID;  // NaN
   if (c->scale_group != 0 && c->scale_group != 64) return COLI_E_INVALID;
+  if (!(c->topp >= 0.0f && c->topp <= 1.0f)) return COLI_E_INVALID;  // NaN included
   if (c->hidden % 128 || c->ffn % 128) return COLI_E_UNSUPPORTED;
   if (c->n_experts > 1024 || c->n_group > 64 || c->top_k > 64) return COLI_E_UNSUPPORTED;
   if (gemv_lds(c->hidden) > GEMV_LDS_LIMIT || gemv_lds(c->ffn) > GEMV_LDS_LIMIT) return COLI_E_UNSUPPORTED;

@@ -1330,7 +1330,9 @@ hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s) { return launc
 
 // out[t] = sum_j w[t][j] * ypair[t*k + j] (j ascending) + ypair[P + t] (shared).
 // The slots are loaded eight at a time (independent loads in flight together) and
-// added in ascending order, so the result does not depend on the batching.
+// added in ascending order, so the result does not depend on the batching. A slot
+// of weight 0 is an empty slot (adaptive top-p: its pair row was never written) and
+// is not added; a kept slot's weight is never 0 (sigmoid scores are positive).
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ypair, const float *__restrict__ w,
                                                       int T, int k, int H, int has_shared,
                                                       float *__restrict__ out) {
@@ -1353,7 +1355,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     }
 #pragma unroll
     for (int j = 0; j < JB; j++) {
-      if (j0 + j < k) {
+      if (j0 + j < k && wj[j] != 0.0f) {
         acc.x += wj[j] * y[j].x;
         acc.y += wj[j] * y[j].y;
         acc.z += wj[j] * y[j].z;

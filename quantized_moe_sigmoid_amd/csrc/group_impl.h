@@ -45,7 +45,7 @@ __device__ __forceinline__ void group_rank_chunk(const int32_t *__restrict__ idx
     if (p < P) {
       e = idx[p];
       if (e < 0 || e >= E) {
-        bad = 1;
+        if (e != -1) bad = 1;  // -1: an empty slot (adaptive top-p), part of no expert
         e = -1;
       }
     }

@@ -298,6 +298,7 @@ struct SelectArgs {
   const double *part;
   int ksplit, T, E, G, Gk, k;
   float rsf;
+  float topp;  // 0: plain top-k; else adaptive expert top-p
   const float *bias;
   int32_t *idx;
   float *w;
@@ -474,9 +475,29 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   if (tid < k) {
     double S = 0.0;
     for (int j = 0; j < k; j++) S += sel_s[j];
-    const int e = sel_e[tid];
+    int kept = k;
+    if (a.topp > 0.0f) {
+      // adaptive top-p: the shortest prefix of the slots whose scores reach topp * S;
+      // its sum (same order) renormalises the kept weights
+      const double target = (double)a.topp * S;
+      double cum = 0.0;
+      for (int j = 0; j < k; j++) {
+        cum += sel_s[j];
+        if (cum >= target) {
+          kept = j + 1;
+          break;
+        }
+      }
+      S = cum;
+    }
+    int e = sel_e[tid];
+    float wt = (e >= 0) ? (float)((sel_s[tid] / S) * (double)a.rsf) : 0.0f;
+    if (tid >= kept) {
+      e = -1;
+      wt = 0.0f;
+    }
     a.idx[(int64_t)t * k + tid] = e;
-    a.w[(int64_t)t * k + tid] = (e >= 0) ? (float)((sel_s[tid] / S) * (double)a.rsf) : 0.0f;
+    a.w[(int64_t)t * k + tid] = wt;
   }
 }
 
@@ -525,6 +546,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.Gk = c.topk_group;
   a.k = c.top_k;
   a.rsf = c.routed_scaling_factor;
+  a.topp = c.topp;
   a.bias = r.bias;
   a.idx = r.idx;
   a.w = r.w;
