@@ -58,7 +58,8 @@ def read_traffic(workload: str, T: int):
 class Stack:
     """L stacked layers of one workload, resident on the device."""
 
-    def __init__(self, wl_index: int, layers: int, wbits: int | None = None, scale_group: int = 0):
+    def __init__(self, wl_index: int, layers: int, wbits: int | None = None, scale_group: int = 0,
+                 topp: float = 0.0):
         import numpy as np
         import torch
         import quantized_moe_sigmoid_amd as q
@@ -71,6 +72,9 @@ class Stack:
         if scale_group:
             self.wl["scale_group"] = scale_group
             self.wl["name"] += f"_gs{scale_group}"
+        if topp:
+            self.wl["topp"] = topp
+            self.wl["name"] += f"_topp{topp:g}"
         wl = self.wl
         self.cfg = q.make_cfg(**wl)
         self.blob = q.blob_bytes(self.cfg)
@@ -101,7 +105,8 @@ class Stack:
         return xs
 
     def union_sizes(self, xs):
-        """Distinct routed experts U of each layer for these inputs (from the library's own grouping)."""
+        """Distinct routed experts U of each layer for these inputs, and the routed pairs kept
+        (fewer than T * k with adaptive top-p), from the library's own route and grouping."""
         import torch
         import quantized_moe_sigmoid_amd as q
         T = xs[0].shape[0]
@@ -114,12 +119,13 @@ class Stack:
         perm = torch.empty(T * k, dtype=torch.int32, device=self.dev)
         act = torch.empty(E, dtype=torch.int32, device=self.dev)
         na = torch.empty(1, dtype=torch.int32, device=self.dev)
-        us = []
+        us, pairs = [], []
         for (seed, w), x in zip(self.layers, xs):
             q.route(self.cfg, w, x, idx, tw, ws)
             q.group(self.cfg, idx, T, cnt, off, perm, act, na)
             us.append(int(na.item()))
-        return us
+            pairs.append(int(off[E].item()))
+        return us, pairs
 
 
 def _row_scale_bytes(wl, n_inputs: int) -> int:
@@ -128,7 +134,7 @@ def _row_scale_bytes(wl, n_inputs: int) -> int:
     return 4 if g == 0 else 4 * (n_inputs // g)
 
 
-def gateup_bytes(wl, U: int, T: int) -> int:
+def gateup_bytes(wl, U: int, T: int, pairs: int | None = None) -> int:
     """Algorithmic HBM bytes of one gate/up launch: the packed gate and up rows plus their
     fp32 scales of the U routed (+ shared) experts, the Q8_0 activations read once, and
     the requantised h written once."""
@@ -137,7 +143,7 @@ def gateup_bytes(wl, U: int, T: int) -> int:
     nexp = U + S
     weights = nexp * 2 * F * (H * wb // 8 + _row_scale_bytes(wl, H))
     acts = T * (H + 8 * (H // 32))
-    rows_out = T * k + S * T
+    rows_out = (T * k if pairs is None else pairs) + S * T
     hout = rows_out * (F + 8 * (F // 32))
     return weights + acts + hout
 
@@ -207,8 +213,8 @@ def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
                 acc[s] += ev.elapsed_ms(s, s + 1)
     ev.close()
     stage_ms = {names[s]: acc[s] / nprof for s in range(ns)}
-    us = stack.union_sizes(xs)
-    return dict(T=T, ms=ms, steps=nsteps, stage_ms=stage_ms, U=us)
+    us, pairs = stack.union_sizes(xs)
+    return dict(T=T, ms=ms, steps=nsteps, stage_ms=stage_ms, U=us, pairs=pairs)
 
 
 def copy_bandwidth(mbytes: int, reps: int):
@@ -233,10 +239,10 @@ def copy_bandwidth(mbytes: int, reps: int):
     return 2 * n / dt / 1e9
 
 
-def gateup_ops(wl, T: int) -> int:
+def gateup_ops(wl, T: int, pairs: float | None = None) -> int:
     """int8 multiply-add operations (x2) of one gate/up launch: every (token, expert)
     pair and every shared-expert row against 2F weight rows of H inputs."""
-    rows = T * wl["top_k"] + (T if wl["has_shared"] else 0)
+    rows = (T * wl["top_k"] if pairs is None else pairs) + (T if wl["has_shared"] else 0)
     return 2 * rows * 2 * wl["ffn"] * wl["hidden"]
 
 
@@ -341,6 +347,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--wbits", type=int, default=None)
+    ap.add_argument("--topp", type=float, default=0.0,
+                    help="adaptive expert top-p (0: plain top-k); changes the router's result")
     ap.add_argument("--scale-group", type=int, default=0, choices=[0, 64],
                     help="64: group-scaled weights, one fp32 scale per 64 inputs of a row")
     ap.add_argument("--tokens", type=str, default=None, help="comma list of T; the last is the headline")
@@ -376,7 +384,7 @@ def main():
         log(f"copy kernel ({args.calib_mb} MiB): {copy_gbs:.0f} GB/s read+write")
     wl0 = synth.WORKLOADS[args.config]
     Ts = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl0["tokens"])
-    stack = Stack(args.config, args.layers, args.wbits, args.scale_group)
+    stack = Stack(args.config, args.layers, args.wbits, args.scale_group, args.topp)
     wl = stack.wl
     results = []
     for T in Ts:
@@ -386,7 +394,7 @@ def main():
         r["tok_s"] = T / (r["ms"] * 1e-3)
         gu_ms = r["stage_ms"][DOMINANT_STAGE]
         # algorithmic bytes of the dominant kernel per launch, averaged over the stacked layers
-        gb = sum(gateup_bytes(wl, u, T) for u in r["U"]) / len(r["U"])
+        gb = sum(gateup_bytes(wl, u, T, pr) for u, pr in zip(r["U"], r["pairs"])) / len(r["U"])
         r["gateup_bytes"] = gb
         r["gateup_gbs"] = gb / (gu_ms * 1e-3) / 1e9
         r["layer_weight_gbs"] = (sum(layer_weight_bytes(wl, u) for u in r["U"]) / len(r["U"])) / (r["ms"] * 1e-3) / 1e9
@@ -400,7 +408,7 @@ def main():
     gu_ms = head["stage_ms"][DOMINANT_STAGE]
     traffic = read_traffic(wl["name"], T)
     if gemm:
-        ops = gateup_ops(wl, T)
+        ops = int(gateup_ops(wl, T, sum(head["pairs"]) / len(head["pairs"])))
         ach = ops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic,
@@ -435,12 +443,13 @@ def main():
         "config": {"workload": wl["name"], "hidden": wl["hidden"], "ffn": wl["ffn"], "n_experts": wl["n_experts"],
                    "top_k": wl["top_k"], "n_group": wl["n_group"], "topk_group": wl["topk_group"],
                    "has_shared": wl["has_shared"], "wbits": wl["wbits"],
-                   "scale_group": wl.get("scale_group", 0), "tokens": T,
+                   "scale_group": wl.get("scale_group", 0), "topp": wl.get("topp", 0.0), "tokens": T,
                    "stacked_layers": stack.L, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": [{"T": r["T"], "tokens_per_s": round(r["tok_s"], 1), "us_per_step": round(r["ms"] * 1e3, 2),
-                   "U_mean": r["U_mean"], "gate_up_GBps": round(r["gateup_gbs"], 1),
+                   "U_mean": r["U_mean"], "pairs_mean": sum(r["pairs"]) / len(r["pairs"]),
+                   "gate_up_GBps": round(r["gateup_gbs"], 1),
                    "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
                    "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}} for r in results],
     }
