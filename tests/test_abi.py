@@ -64,6 +64,10 @@ BAD_CFGS = [
     (dict(hidden=256, ffn=96, n_experts=16, top_k=4), -2),                             # F % 128
     (dict(hidden=256, ffn=128, n_experts=2048, top_k=4), -2),                          # E > 1024
     (dict(hidden=16384, ffn=128, n_experts=16, top_k=4), -2),                          # LDS of the GEMV
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, scale_group=32), -1),            # group size 64 only
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=1.5), -1),                  # topp in [0, 1]
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=-0.1), -1),
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=float("nan")), -1),
 ]
 
 
@@ -74,6 +78,7 @@ def test_bad_config_rejected(q, cfgd, want):
     w = _w(q)
     p = C.c_void_p(FAKE)
     assert L.coli_moe_blob_bytes(C.byref(c)) == 0
+    assert L.coli_moe_scales_per_expert(C.byref(c)) == 0
     assert L.coli_moe_workspace_bytes(C.byref(c), 8) == 0
     assert L.coli_moe_layer(C.byref(c), C.byref(w), p, 8, p, None, None, p, 1 << 30, None) == want
     assert L.coli_moe_route(C.byref(c), C.byref(w), p, 8, p, p, p, 1 << 30, None) == want
