@@ -12,6 +12,7 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+W_MXFP4 = 40  # wbits value of MXFP4 weights (COLI_REF_W_MXFP4)
 LIB_PATH = os.path.join(HERE, "liboracle_coli.so")
 SOURCES = [os.path.join(HERE, "coli_ref.c")]
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11",
@@ -61,6 +62,7 @@ def lib():
             "coli_ref_expert_ffn": [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P],
             "coli_ref_moe_ffn": [P, P, P, P, i32, P, P, P],
             "coli_ref_moe_layer": [P, P, P, P, P, P, i32, P, P, P],
+            "coli_ref_mxfp4_decode": [P, i64, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -70,6 +72,10 @@ def lib():
         L.coli_ref_row_bytes.restype = C.c_int64
         L.coli_ref_blob_bytes.argtypes = [i32, i32, i32]
         L.coli_ref_blob_bytes.restype = C.c_int64
+        for name in ("coli_ref_e2m1", "coli_ref_e8m0"):
+            f = getattr(L, name)
+            f.argtypes = [C.c_uint32]
+            f.restype = C.c_double
         L.coli_ref_threads.restype = C.c_int
         L.coli_ref_set_threads.argtypes = [C.c_int]
         _lib = L
@@ -82,6 +88,11 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _scales(a, wbits):
+    """Scales as the oracle reads them: fp32, or E8M0 bytes for MXFP4."""
+    return _c(a, np.uint8 if wbits == W_MXFP4 else np.float32)
 
 
 def _check(rc, what):
@@ -121,6 +132,23 @@ def unpack(b, wbits, n):
     return q
 
 
+def e2m1(code: int) -> float:
+    return float(lib().coli_ref_e2m1(int(code)))
+
+
+def e8m0(u: int) -> float:
+    return float(lib().coli_ref_e8m0(int(u)))
+
+
+def mxfp4_decode(b, n):
+    """E2M1 values (unscaled) of n packed MXFP4 codes."""
+    b = _c(b, np.uint8).ravel()
+    assert b.size >= n // 2
+    v = np.empty(n, np.float64)
+    _check(lib().coli_ref_mxfp4_decode(_p(b), n, _p(v)), "mxfp4_decode")
+    return v
+
+
 def route(cfg: Cfg, router_w, router_bias, x, scores=False):
     x = _c(x, np.float32)
     T = x.shape[0]
@@ -150,9 +178,10 @@ def group(cfg: Cfg, idx):
 
 def expert_ffn(hidden, ffn, wbits, blob, scales, xq, xd, scale_group=0):
     """All intermediates of one expert on one Q8_0 row: dict of g, u, h, hq, hd, y.
-    scales: one per row (scale_group 0) or one per 64 inputs of a row (scale_group 64)."""
+    scales: one per row (scale_group 0) or one per 64 inputs of a row (scale_group 64), fp32;
+    MXFP4 (wbits W_MXFP4, scale_group 32): one E8M0 byte per 32 inputs of a row."""
     blob = _c(blob, np.uint8)
-    scales = _c(scales, np.float32)
+    scales = _scales(scales, wbits)
     xq = _c(xq, np.int8)
     xd = _c(xd, np.float32)
     g = np.empty(ffn, np.float64)
@@ -170,7 +199,7 @@ def ffn(cfg: Cfg, blobs, scales, x, idx, w):
     x = _c(x, np.float32)
     T = x.shape[0]
     out = np.empty((T, cfg.hidden), np.float32)
-    _check(lib().coli_ref_moe_ffn(C.byref(cfg), _p(_c(blobs, np.uint8)), _p(_c(scales, np.float32)), _p(x), T,
+    _check(lib().coli_ref_moe_ffn(C.byref(cfg), _p(_c(blobs, np.uint8)), _p(_scales(scales, cfg.wbits)), _p(x), T,
                                   _p(_c(idx, np.int32)), _p(_c(w, np.float32)), _p(out)), "ffn")
     return out
 
@@ -181,7 +210,7 @@ def layer(cfg: Cfg, blobs, scales, router_w, router_bias, x):
     out = np.empty((T, cfg.hidden), np.float32)
     idx = np.empty((T, cfg.top_k), np.int32)
     w = np.empty((T, cfg.top_k), np.float32)
-    _check(lib().coli_ref_moe_layer(C.byref(cfg), _p(_c(blobs, np.uint8)), _p(_c(scales, np.float32)),
+    _check(lib().coli_ref_moe_layer(C.byref(cfg), _p(_c(blobs, np.uint8)), _p(_scales(scales, cfg.wbits)),
                                     _p(_c(router_w, np.float32)), _p(_c(router_bias, np.float32)), _p(x), T,
                                     _p(out), _p(idx), _p(w)), "layer")
     return out, idx, w

@@ -38,7 +38,9 @@ void coli_ref_set_threads(int n) {
 }
 
 int64_t coli_ref_row_bytes(int32_t wbits, int32_t n) {
-  if ((wbits != 2 && wbits != 4 && wbits != 8) || n <= 0 || n % QK) return -1;
+  if (n <= 0 || n % QK) return -1;
+  if (wbits == COLI_REF_W_MXFP4) return (int64_t)n / 2; /* 4-bit codes; the scales are stored apart */
+  if (wbits != 2 && wbits != 4 && wbits != 8) return -1;
   return (int64_t)n * wbits / 8;
 }
 
@@ -148,6 +150,33 @@ int coli_ref_unpack(int32_t wbits, const uint8_t *in, int64_t n, int8_t *q) {
   return 0;
 }
 
+/* ------------------------------------------------------------------ MXFP4 --
+ * The element and scale encodings of the OCP MX formats (the pages name MXFP4
+ * experts without spelling the format out): E2M1 has one sign bit, two exponent
+ * bits of bias 1 and one mantissa bit; exponent field 0 holds the subnormals 0 and
+ * 1/2. E8M0 is a bare biased exponent, 2^(u - 127), with u = 255 reserved for NaN. */
+double coli_ref_e2m1(uint32_t code) {
+  const uint32_t sgn = (code >> 3) & 1u, ex = (code >> 1) & 3u, man = code & 1u;
+  const double mag = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, (int)ex - 1);
+  return sgn ? -mag : mag;
+}
+
+double coli_ref_e8m0(uint32_t u) {
+  if (u > 255) return NAN;
+  return u == 255 ? NAN : ldexp(1.0, (int)u - 127);
+}
+
+int coli_ref_mxfp4_decode(const uint8_t *in, int64_t n, double *v) {
+  if (!in || !v || n < 0 || n % QK) return -1;
+  for (int64_t b = 0; b < n / QK; b++)
+    for (int j = 0; j < 16; j++) {
+      const unsigned byte = in[b * 16 + j];
+      v[b * QK + j] = coli_ref_e2m1(byte & 0xFu);
+      v[b * QK + j + 16] = coli_ref_e2m1(byte >> 4);
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------------ router --
  * colibri-strix README, "What's implemented", router item: DeepSeek-V3-style
  * sigmoid router, noaux_tc, routed_scaling_factor. The pages name the scheme
@@ -165,9 +194,9 @@ static int cfg_ok(const coli_ref_cfg *c) {
   if (c->n_experts <= 0 || c->n_group <= 0 || c->n_experts % c->n_group) return 0;
   if (c->topk_group < 1 || c->topk_group > c->n_group) return 0;
   if (c->top_k < 1 || c->top_k > c->topk_group * (c->n_experts / c->n_group)) return 0;
-  if (c->wbits != 2 && c->wbits != 4 && c->wbits != 8) return 0;
+  if (c->wbits != 2 && c->wbits != 4 && c->wbits != 8 && c->wbits != COLI_REF_W_MXFP4) return 0;
   if (c->has_shared != 0 && c->has_shared != 1) return 0;
-  if (c->scale_group != 0 && c->scale_group != 64) return 0;
+  if (c->wbits == COLI_REF_W_MXFP4 ? c->scale_group != 32 : (c->scale_group != 0 && c->scale_group != 64)) return 0;
   if (c->scale_group && (c->hidden % c->scale_group || c->ffn % c->scale_group)) return 0;
   if (!(c->topp >= 0.0f && c->topp <= 1.0f)) return 0;
   return 1;
@@ -336,6 +365,23 @@ static double row_dot(const int8_t *wrow, const int8_t *aq, const float *ad, int
   return acc;
 }
 
+/* MXFP4 row: the weight is e2m1(code) * 2^(u_b - 127) with one scale byte u_b per
+ * 32-value block, so a row's dot is sum_b d_b * 2^(u_b - 127) * J_b, J_b = sum over the
+ * block of xq * e2m1 (a multiple of 1/2, exact in double). */
+static double mx_row_dot(const uint8_t *row, const uint8_t *u, const int8_t *aq, const float *ad, int32_t n) {
+  double acc = 0.0;
+  for (int32_t b = 0; b < n / QK; b++) {
+    double j = 0.0;
+    for (int i = 0; i < 16; i++) {
+      const unsigned byte = row[(int64_t)b * 16 + i];
+      j += (double)aq[(int64_t)b * QK + i] * coli_ref_e2m1(byte & 0xFu);
+      j += (double)aq[(int64_t)b * QK + i + 16] * coli_ref_e2m1(byte >> 4);
+    }
+    acc += (double)ad[b] * coli_ref_e8m0(u[b]) * j;
+  }
+  return acc;
+}
+
 /* The scaled dot of one row: s[0] * row_dot with one scale per row (gs = 0), else
  * sum over the n / gs groups of s[grp] * (the row_dot of that group's inputs). */
 static double scaled_row_dot(const int8_t *wrow, const int8_t *aq, const float *ad, int32_t n, int32_t gs,
@@ -348,16 +394,18 @@ static double scaled_row_dot(const int8_t *wrow, const int8_t *aq, const float *
 }
 
 int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scale_group, const uint8_t *blob,
-                        const float *scales, const int8_t *xq, const float *xd,
+                        const void *scales, const int8_t *xq, const float *xd,
                         double *g_out, double *u_out, float *h_out, int8_t *hq_out, float *hd_out,
                         double *y_out) {
   const int64_t rh = coli_ref_row_bytes(wbits, hidden), rf = coli_ref_row_bytes(wbits, ffn);
   if (rh < 0 || rf < 0 || !blob || !scales || !xq || !xd) return -1;
-  if (scale_group != 0 && (scale_group != 64 || hidden % 64 || ffn % 64)) return -1;
+  const int mx = wbits == COLI_REF_W_MXFP4;
+  if (mx ? scale_group != 32 : (scale_group != 0 && (scale_group != 64 || hidden % 64 || ffn % 64))) return -1;
   const int32_t H = hidden, F = ffn, gs = scale_group;
   /* scales of one row of each matrix: per-row index, or [row][group] */
   const int64_t sgh = gs ? H / gs : 1, sgf = gs ? F / gs : 1;
-  const float *sg = scales, *su = scales + (int64_t)F * sgh, *sd = scales + 2 * (int64_t)F * sgh;
+  const float *sg = scales, *su = sg + (int64_t)F * sgh, *sd = sg + 2 * (int64_t)F * sgh;
+  const uint8_t *ug = scales, *uu = ug + (int64_t)F * sgh, *ud = ug + 2 * (int64_t)F * sgh; /* MXFP4 */
   int8_t *wrow = malloc((size_t)(H > F ? H : F));
   float *h = malloc(sizeof(float) * (size_t)F);
   int8_t *hq = malloc((size_t)F);
@@ -368,10 +416,16 @@ int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scal
   }
   const uint8_t *gate = blob, *up = blob + (int64_t)F * rh, *down = blob + 2 * (int64_t)F * rh;
   for (int32_t f = 0; f < F; f++) {
-    coli_ref_unpack(wbits, gate + (int64_t)f * rh, H, wrow);
-    double g = scaled_row_dot(wrow, xq, xd, H, gs, sg + f * sgh);
-    coli_ref_unpack(wbits, up + (int64_t)f * rh, H, wrow);
-    double u = scaled_row_dot(wrow, xq, xd, H, gs, su + f * sgh);
+    double g, u;
+    if (mx) {
+      g = mx_row_dot(gate + (int64_t)f * rh, ug + f * sgh, xq, xd, H);
+      u = mx_row_dot(up + (int64_t)f * rh, uu + f * sgh, xq, xd, H);
+    } else {
+      coli_ref_unpack(wbits, gate + (int64_t)f * rh, H, wrow);
+      g = scaled_row_dot(wrow, xq, xd, H, gs, sg + f * sgh);
+      coli_ref_unpack(wbits, up + (int64_t)f * rh, H, wrow);
+      u = scaled_row_dot(wrow, xq, xd, H, gs, su + f * sgh);
+    }
     h[f] = (float)(g / (1.0 + exp(-g)) * u);
     if (g_out) g_out[f] = g;
     if (u_out) u_out[f] = u;
@@ -379,8 +433,12 @@ int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scal
   coli_ref_quantize_q8_0(h, 1, F, hq, hd);
   if (y_out)
     for (int32_t r = 0; r < H; r++) {
-      coli_ref_unpack(wbits, down + (int64_t)r * rf, F, wrow);
-      y_out[r] = scaled_row_dot(wrow, hq, hd, F, gs, sd + r * sgf);
+      if (mx) {
+        y_out[r] = mx_row_dot(down + (int64_t)r * rf, ud + r * sgf, hq, hd, F);
+      } else {
+        coli_ref_unpack(wbits, down + (int64_t)r * rf, F, wrow);
+        y_out[r] = scaled_row_dot(wrow, hq, hd, F, gs, sd + r * sgf);
+      }
     }
   if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)F);
   if (hq_out) memcpy(hq_out, hq, (size_t)F);
@@ -395,7 +453,7 @@ int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scal
  * rounded once to fp32. The shared expert is always applied (colibri-strix
  * README, "What's implemented", router item; "The idea": shared experts are part
  * of the dense, always-resident set). */
-int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const float *scales,
+int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const void *scales,
                      const float *x, int32_t T, const int32_t *topk_idx, const float *topk_w,
                      float *out) {
   if (!cfg_ok(cfg) || T < 0 || !experts || !scales) return -1;
@@ -405,6 +463,7 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
   const int64_t blob = coli_ref_blob_bytes(H, F, cfg->wbits);
   const int32_t gs = cfg->scale_group;
   const int64_t srow = gs ? 3 * (int64_t)F * (H / gs) : 2 * (int64_t)F + H;  /* scales per expert */
+  const int64_t sbytes = srow * (cfg->wbits == COLI_REF_W_MXFP4 ? 1 : (int64_t)sizeof(float));
   for (int64_t p = 0; p < (int64_t)T * k; p++)
     if (topk_idx[p] < -1 || topk_idx[p] >= E) return -2;  /* -1: empty slot (adaptive top-p) */
   const int nslot = k + (cfg->has_shared ? 1 : 0);
@@ -424,8 +483,8 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
         for (int j = 0; j < nslot; j++) {
           int64_t e = j < k ? topk_idx[(int64_t)t * k + j] : E; /* shared expert stored after the routed ones */
           if (e < 0) continue;                                  /* empty slot: weight 0, never read */
-          coli_ref_expert_ffn(H, F, cfg->wbits, gs, experts + e * blob, scales + e * srow, xq, xd, NULL, NULL,
-                              NULL, NULL, NULL, y + (int64_t)j * H);
+          coli_ref_expert_ffn(H, F, cfg->wbits, gs, experts + e * blob, (const uint8_t *)scales + e * sbytes, xq, xd,
+                              NULL, NULL, NULL, NULL, NULL, y + (int64_t)j * H);
         }
         for (int32_t r = 0; r < H; r++) {
           double acc = 0.0;
@@ -441,7 +500,7 @@ int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const floa
   return bad ? -3 : 0;
 }
 
-int coli_ref_moe_layer(const coli_ref_cfg *cfg, const uint8_t *experts, const float *scales,
+int coli_ref_moe_layer(const coli_ref_cfg *cfg, const uint8_t *experts, const void *scales,
                        const float *router_w, const float *router_bias, const float *x, int32_t T,
                        float *out, int32_t *topk_idx_opt, float *topk_w_opt) {
   if (!cfg_ok(cfg) || T < 0) return -1;

@@ -46,10 +46,28 @@ typedef struct {
   int32_t topk_group;   /* Gk, 1 <= Gk <= G */
   float   rsf;          /* routed_scaling_factor */
   int32_t has_shared;   /* 0/1: shared expert stored after the routed ones */
-  int32_t wbits;        /* 2, 4 or 8 */
-  int32_t scale_group;  /* 0: one fp32 scale per row; 64: one per 64 consecutive inputs of a row */
+  int32_t wbits;        /* 2, 4, 8, or COLI_REF_W_MXFP4 */
+  int32_t scale_group;  /* 0: one fp32 scale per row; 64: one per 64 consecutive inputs of a row;
+                           32 (and only 32) with COLI_REF_W_MXFP4: one E8M0 byte per block */
   float   topp;         /* 0: plain top-k; 0 < topp <= 1: adaptive expert top-p (see coli_ref_moe_route) */
 } coli_ref_cfg;
+
+/* MXFP4 weights (the Kimi K3 / DeepSeek V4 expert format named on the JustVugg/colibri
+ * README, "Other supported models"; the pages name it only, so the element and scale
+ * encodings are the OCP Microscaling (MX) v1.0 ones): blocks of 32 E2M1 codes sharing
+ * one E8M0 scale byte. A code c = s e1 e0 m (bit 3 .. bit 0) is (-1)^s * 2^(e - 1) *
+ * (1 + m / 2) for e > 0 and (-1)^s * m / 2 for e = 0; a scale byte u is 2^(u - 127),
+ * and u = 255 is NaN. Packed as int4 (code j in the low nibble of byte j, code j + 16 in
+ * the high nibble, per block); scales per expert: gate [F][H/32] | up [F][H/32] |
+ * down [H][F/32] bytes. */
+#define COLI_REF_W_MXFP4 40
+
+/* Value of one E2M1 code (0..15) and of one E8M0 byte. */
+double coli_ref_e2m1(uint32_t code);
+double coli_ref_e8m0(uint32_t u);
+
+/* E2M1 values of n packed codes (n % 32 == 0), in value order. */
+int coli_ref_mxfp4_decode(const uint8_t *in, int64_t n, double *v);
 
 /* Q8_0 of rows x cols fp32 values (cols % 32 == 0): q int8 [rows, cols], d fp32 [rows, cols/32]. */
 int coli_ref_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d);
@@ -82,21 +100,23 @@ int coli_ref_moe_group(const coli_ref_cfg *cfg, const int32_t *topk_idx, int32_t
 /* One expert applied to one Q8_0 activation row, with every intermediate.
  * blob: gate[F] | up[F] | down[H] packed rows. scales (fp32): with scale_group 0,
  * [2F + H] one per row (gate rows, up rows, down rows); with scale_group 64, one
- * per 64 inputs of a row, gate [F][H/64] | up [F][H/64] | down [H][F/64].
+ * per 64 inputs of a row, gate [F][H/64] | up [F][H/64] | down [H][F/64]; with
+ * MXFP4 weights, E8M0 bytes, one per 32 inputs of a row in the same order.
  * Outputs (any may be NULL): g, u double [F]; h fp32 [F]; hq int8 [F];
  * hd fp32 [F/32]; y double [H]. */
 int coli_ref_expert_ffn(int32_t hidden, int32_t ffn, int32_t wbits, int32_t scale_group, const uint8_t *blob,
-                        const float *scales, const int8_t *xq, const float *xd,
+                        const void *scales, const int8_t *xq, const float *xd,
                         double *g, double *u, float *h, int8_t *hq, float *hd, double *y);
 
 /* Expert FFNs and combine for given routing. experts: (E + has_shared) blobs of
- * blob stride bytes; scales: (E + has_shared) x (2F + H) fp32. out fp32 [T, H]. */
-int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const float *scales,
+ * blob stride bytes; scales: (E + has_shared) x (scales of one expert, as above; fp32,
+ * or bytes for MXFP4). out fp32 [T, H]. */
+int coli_ref_moe_ffn(const coli_ref_cfg *cfg, const uint8_t *experts, const void *scales,
                      const float *x, int32_t T, const int32_t *topk_idx, const float *topk_w,
                      float *out);
 
 /* Whole layer: route, then FFN and combine. */
-int coli_ref_moe_layer(const coli_ref_cfg *cfg, const uint8_t *experts, const float *scales,
+int coli_ref_moe_layer(const coli_ref_cfg *cfg, const uint8_t *experts, const void *scales,
                        const float *router_w, const float *router_bias, const float *x, int32_t T,
                        float *out, int32_t *topk_idx_opt, float *topk_w_opt);
 

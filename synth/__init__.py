@@ -93,9 +93,12 @@ def normal(key: int, n: int, std: float = 1.0) -> np.ndarray:
     return z[:n] * std
 
 
+W_MXFP4 = 40  # wbits value of MXFP4 weights: 4-bit E2M1 codes, E8M0 scale bytes per 32 inputs
+
+
 def row_bytes(n: int, wbits: int) -> int:
     """Packed bytes of one weight row with n inputs (n multiple of 32)."""
-    return n * wbits // 8
+    return n // 2 if wbits == W_MXFP4 else n * wbits // 8
 
 
 def blob_bytes(hidden: int, ffn: int, wbits: int) -> int:
@@ -129,10 +132,15 @@ def scales_per_expert(hidden: int, ffn: int, scale_group: int = 0) -> int:
     return 2 * ffn + hidden if scale_group == 0 else 3 * ffn * (hidden // scale_group)
 
 
-def expert_scales(seed: int, layer: int, expert: int, hidden: int, ffn: int, scale_group: int = 0) -> np.ndarray:
+def expert_scales(seed: int, layer: int, expert: int, hidden: int, ffn: int, scale_group: int = 0,
+                  wbits: int = 4) -> np.ndarray:
     """fp32 scales of one expert, U(0.005, 0.02): per row gate[F], up[F], down[H]; or with
-    group scales gate[F][H/g], up[F][H/g], down[H][F/g]."""
+    group scales gate[F][H/g], up[F][H/g], down[H][F/g]. MXFP4 (scale_group 32): E8M0
+    bytes uniform over 119..122 (2^-8 .. 2^-5, so |w| <= 6 * 2^-5, the range of the
+    integer formats' weights), same order."""
     key = derive_key(seed, TAG_SCALE, layer, expert)
+    if wbits == W_MXFP4:
+        return (119 + (words(key, scales_per_expert(hidden, ffn, scale_group)) & 3)).astype(np.uint8)
     u = uniform01(key, scales_per_expert(hidden, ffn, scale_group))
     return (0.005 + 0.015 * u).astype(np.float32)
 
@@ -176,7 +184,7 @@ def layer_inputs(seed: int, layer: int, *, tokens: int, hidden: int, ffn: int, n
         "x": activations(seed, layer, tokens, hidden, x_index),
         "router_w": router_weight(seed, layer, n_experts, hidden),
         "router_bias": zipf_bias(seed, layer, n_experts) if zipf else router_bias(seed, layer, n_experts),
-        "scales": np.stack([expert_scales(seed, layer, e, hidden, ffn, scale_group) for e in range(ne)]),
+        "scales": np.stack([expert_scales(seed, layer, e, hidden, ffn, scale_group, wbits) for e in range(ne)]),
     }
     if with_blobs:
         d["blobs"] = np.stack([expert_blob(seed, layer, e, hidden, ffn, wbits) for e in range(ne)])

@@ -50,6 +50,35 @@ def dequant_expert(blob, scales, hidden, ffn, wbits, scale_group=0):
     return (gate * sg, up * su, down * sd)
 
 
+# OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element: the sixteen code points and
+# their values, as the specification tabulates them (code 8 is negative zero).
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0)
+
+
+def mxfp4_values_np(packed, n):
+    """E2M1 values of n packed codes by table lookup (code j low nibble, j + 16 high)."""
+    b = np.asarray(packed, np.uint8).reshape(-1)[: n // 2].reshape(-1, 16)
+    codes = np.concatenate([b & 0xF, b >> 4], axis=1).reshape(-1)
+    return np.asarray(E2M1_VALUES, np.float64)[codes]
+
+
+def dequant_expert_mxfp4(blob, scales, hidden, ffn):
+    """Dense float64 gate, up [F, H] and down [H, F] of an MXFP4 expert:
+    e2m1(code) * 2^(u - 127) with one scale byte u per 32 inputs of a row."""
+    rh, rf = hidden // 2, ffn // 2
+    blob = np.asarray(blob, np.uint8)
+    u = np.asarray(scales, np.uint8).astype(np.int64)
+    pw = np.ldexp(1.0, u - 127)
+    ng, nd = ffn * (hidden // 32), hidden * (ffn // 32)
+    gate = mxfp4_values_np(blob[: ffn * rh], ffn * hidden).reshape(ffn, hidden)
+    up = mxfp4_values_np(blob[ffn * rh: 2 * ffn * rh], ffn * hidden).reshape(ffn, hidden)
+    down = mxfp4_values_np(blob[2 * ffn * rh: 2 * ffn * rh + hidden * rf], hidden * ffn).reshape(hidden, ffn)
+    sg = np.repeat(pw[:ng].reshape(ffn, hidden // 32), 32, axis=1)
+    su = np.repeat(pw[ng: 2 * ng].reshape(ffn, hidden // 32), 32, axis=1)
+    sd = np.repeat(pw[2 * ng: 2 * ng + nd].reshape(hidden, ffn // 32), 32, axis=1)
+    return gate * sg, up * su, down * sd
+
+
 def dequant_q8(q, d):
     """Dequantised Q8_0 row: d[block] * q in float64."""
     q = np.asarray(q, np.float64).reshape(-1, 32)
