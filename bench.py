@@ -69,9 +69,13 @@ class Stack:
         self.wl = dict(synth.WORKLOADS[wl_index])
         if wbits is not None:
             self.wl["wbits"] = wbits
+        if wbits == synth.W_MXFP4:  # MXFP4: E8M0 scale bytes, one per 32 inputs
+            scale_group = 32
+            self.wl["name"] += "_mxfp4"
         if scale_group:
             self.wl["scale_group"] = scale_group
-            self.wl["name"] += f"_gs{scale_group}"
+            if scale_group != 32:
+                self.wl["name"] += f"_gs{scale_group}"
         if topp:
             self.wl["topp"] = topp
             self.wl["name"] += f"_topp{topp:g}"
@@ -128,9 +132,17 @@ class Stack:
         return us, pairs
 
 
+def _packed_row_bytes(wl, n_inputs: int) -> int:
+    """Packed weight bytes of one row (MXFP4: 4-bit codes)."""
+    return n_inputs // 2 if wl["wbits"] == 40 else n_inputs * wl["wbits"] // 8
+
+
 def _row_scale_bytes(wl, n_inputs: int) -> int:
-    """fp32 scale bytes of one weight row of n_inputs: one per row, or one per group."""
+    """Scale bytes of one weight row of n_inputs: one fp32 per row or per group; MXFP4 one
+    E8M0 byte per 32 inputs."""
     g = wl.get("scale_group", 0)
+    if wl["wbits"] == 40:
+        return n_inputs // 32
     return 4 if g == 0 else 4 * (n_inputs // g)
 
 
@@ -138,10 +150,10 @@ def gateup_bytes(wl, U: int, T: int, pairs: int | None = None) -> int:
     """Algorithmic HBM bytes of one gate/up launch: the packed gate and up rows plus their
     fp32 scales of the U routed (+ shared) experts, the Q8_0 activations read once, and
     the requantised h written once."""
-    H, F, k, wb = wl["hidden"], wl["ffn"], wl["top_k"], wl["wbits"]
+    H, F, k = wl["hidden"], wl["ffn"], wl["top_k"]
     S = 1 if wl["has_shared"] else 0
     nexp = U + S
-    weights = nexp * 2 * F * (H * wb // 8 + _row_scale_bytes(wl, H))
+    weights = nexp * 2 * F * (_packed_row_bytes(wl, H) + _row_scale_bytes(wl, H))
     acts = T * (H + 8 * (H // 32))
     rows_out = (T * k if pairs is None else pairs) + S * T
     hout = rows_out * (F + 8 * (F // 32))
@@ -150,9 +162,10 @@ def gateup_bytes(wl, U: int, T: int, pairs: int | None = None) -> int:
 
 def layer_weight_bytes(wl, U: int) -> int:
     """Packed weights + per-row scales of the experts one layer call streams."""
-    H, F, wb = wl["hidden"], wl["ffn"], wl["wbits"]
+    H, F = wl["hidden"], wl["ffn"]
     nexp = U + (1 if wl["has_shared"] else 0)
-    return nexp * (2 * F * (H * wb // 8 + _row_scale_bytes(wl, H)) + H * (F * wb // 8 + _row_scale_bytes(wl, F)))
+    return nexp * (2 * F * (_packed_row_bytes(wl, H) + _row_scale_bytes(wl, H)) +
+                   H * (_packed_row_bytes(wl, F) + _row_scale_bytes(wl, F)))
 
 
 def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
@@ -346,7 +359,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
-    ap.add_argument("--wbits", type=int, default=None)
+    ap.add_argument("--wbits", type=int, default=None, choices=[2, 4, 8, 40],
+                    help="weight format: int2/int4/int8, or 40 = MXFP4 (E2M1 codes, E8M0 scale per 32 inputs)")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="adaptive expert top-p (0: plain top-k); changes the router's result")
     ap.add_argument("--scale-group", type=int, default=0, choices=[0, 64],
@@ -438,7 +452,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xint4",
+        "dtype": "int8x" + {2: "int2", 4: "int4", 8: "int8", 40: "mxfp4"}[wl["wbits"]],
         "data": "synthetic (seeded SplitMix64; random int weights, N(0,1) activations)",
         "config": {"workload": wl["name"], "hidden": wl["hidden"], "ffn": wl["ffn"], "n_experts": wl["n_experts"],
                    "top_k": wl["top_k"], "n_group": wl["n_group"], "topk_group": wl["topk_group"],

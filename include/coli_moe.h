@@ -40,12 +40,21 @@
  *                (Group scales: JustVugg/colibri README, "2. Get the model", the gs64
  *                int4 container; the pages fix neither the scale type nor the layout,
  *                this library reads them as fp32 in that order.)
+ *                MXFP4 (wfmt COLI_W_MXFP4, scale_group 32): bytes, not fp32: one E8M0
+ *                code u per 32 inputs of a row, gate [F][H/32] | up [F][H/32] |
+ *                down [H][F/32]; expert i's bytes start at i * coli_moe_scales_per_expert.
  *   router_w     fp32 [E][H];  router_bias fp32 [E] (noaux_tc correction bias).
  *   Packed row of n inputs = n/32 blocks of 32 values, two's complement:
  *     int8 (wfmt 8): 32 bytes/block, byte i = value i;
  *     int4 (wfmt 4): 16 bytes/block, byte j = value j | value (j+16) << 4;
- *     int2 (wfmt 2):  8 bytes/block, byte j = sum_m value (j+8m) << 2m, m = 0..3.
- *   Dequantised weight = scale[row] * value, or scale[row][input / 64] * value.
+ *     int2 (wfmt 2):  8 bytes/block, byte j = sum_m value (j+8m) << 2m, m = 0..3;
+ *     MXFP4 (wfmt COLI_W_MXFP4): 16 bytes/block of 4-bit E2M1 codes, byte j = code j |
+ *       code (j+16) << 4.
+ *   Dequantised weight = scale[row] * value, or scale[row][input / 64] * value; MXFP4:
+ *   e2m1(code) * 2^(u - 127) with the block's scale byte u (u = 255 is NaN).
+ *   (MXFP4: the Kimi K3 / DeepSeek V4 expert format of JustVugg/colibri README, "Other
+ *   supported models"; the pages name it only, so the encodings are OCP MX v1.0's:
+ *   E2M1 = sign, two exponent bits of bias 1, one mantissa bit; E8M0 = 2^(u - 127).)
  *
  * Numerics (the readings):
  *   Q8_0: per 32-value block d = max|x| / 127 (one fp32 division, stored fp32),
@@ -57,7 +66,9 @@
  *     descending order; every tie goes to the lower index;
  *     w_j = (float)(s_j / sum_j s_j * rsf), the sum taken in slot order.
  *   Expert (SwiGLU): g = s_gate * sum_b xd_b * I_b (group scales: sum_b s_gate,b/2 *
- *     xd_b * I_b, a 32-value block lying inside one group), u likewise with the up rows,
+ *     xd_b * I_b, a 32-value block lying inside one group; MXFP4: sum_b 2^(u_b - 127) *
+ *     xd_b * J_b with J_b the exact block dot of the codes with their E2M1 values, a
+ *     multiple of 1/2), u likewise with the up rows,
  *     where I_b is the exact int32 dot of block b; h = silu(g) * u in fp32;
  *     hq, hd = Q8_0(h); y = s_down * sum_b hd_b * I_b(hq, down row).
  *   Combine: out_t = sum_j w_tj * y_{e_tj} (j = 0..k-1 in order) + y_shared, fp32,
@@ -82,12 +93,12 @@ typedef enum {
   COLI_E_DEVICE = -5       /* the HIP runtime rejected a launch */
 } coli_status;
 
-typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8 } coli_wfmt;
+typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8, COLI_W_MXFP4 = 40 } coli_wfmt;
 
 /* Layer shape. Limits: hidden and ffn multiples of 128; 1 <= n_experts <= 1024;
  * n_experts % n_group == 0; 1 <= topk_group <= n_group <= 64;
  * 1 <= top_k <= min(64, topk_group * n_experts / n_group); has_shared 0 or 1;
- * wfmt 2, 4 or 8; scale_group 0 or 64; 0 <= topp <= 1. */
+ * wfmt 2, 4, 8 (scale_group 0 or 64) or COLI_W_MXFP4 (scale_group 32); 0 <= topp <= 1. */
 typedef struct {
   int32_t hidden;               /* H */
   int32_t ffn;                  /* F, width of every expert (shared included) */
@@ -98,12 +109,14 @@ typedef struct {
   float routed_scaling_factor;  /* rsf */
   int32_t has_shared;           /* 1: blob E is a shared expert applied to every token */
   int32_t wfmt;                 /* coli_wfmt, one format for all experts of the layer */
-  int32_t scale_group;          /* 0: one scale per weight row; 64: one per 64 inputs of a row */
+  int32_t scale_group;          /* 0: one scale per weight row; 64: one per 64 inputs of a row;
+                                   32: MXFP4's E8M0 byte per 32 inputs (MXFP4 only) */
   float topp;                   /* 0: plain top-k; 0 < topp <= 1: adaptive expert top-p (see the router) */
 } coli_moe_cfg;
 
 /* Device weights of one layer. experts: 16-byte aligned; router_w: 16-byte aligned;
- * scales, router_bias: 4-byte aligned. */
+ * scales, router_bias: 4-byte aligned. scales holds fp32 values, or E8M0 bytes for
+ * MXFP4 (then passed as this pointer type). */
 typedef struct {
   const void *experts;
   const float *scales;
@@ -114,8 +127,8 @@ typedef struct {
 /* Bytes of one packed expert blob (0 if cfg is invalid). */
 size_t coli_moe_blob_bytes(const coli_moe_cfg *cfg);
 
-/* fp32 scales of one expert: 2F + H (scale_group 0) or 3 F H / 64 (scale_group 64);
- * 0 if cfg is invalid. */
+/* Scales of one expert: 2F + H fp32 (scale_group 0), 3 F H / 64 fp32 (scale_group 64),
+ * or 3 F H / 32 E8M0 bytes (MXFP4); 0 if cfg is invalid. */
 size_t coli_moe_scales_per_expert(const coli_moe_cfg *cfg);
 
 /* Workspace bytes that coli_moe_route / coli_moe_ffn / coli_moe_layer need for

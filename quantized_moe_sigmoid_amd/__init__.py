@@ -46,10 +46,13 @@ def make_cfg(hidden, ffn, n_experts, top_k, n_group=1, topk_group=1, rsf=1.0, ha
                topp)
 
 
+W_MXFP4 = 40  # wbits of MXFP4 weights (COLI_W_MXFP4; scale_group 32, E8M0 scale bytes)
+
+
 @dataclass
 class Weights:
-    """Device tensors of one layer: experts uint8 [(E+S) * blob], scales fp32 [(E+S), scales_per_expert],
-    router_w fp32 [E, H], router_bias fp32 [E]."""
+    """Device tensors of one layer: experts uint8 [(E+S) * blob], scales fp32 [(E+S), scales_per_expert]
+    (uint8 E8M0 codes for MXFP4), router_w fp32 [E, H], router_bias fp32 [E]."""
     experts: object
     scales: object
     router_w: object

@@ -15,8 +15,34 @@ constexpr int GEMV_ROWS = 32;       // rows per workgroup tile of the GEMV kerne
 constexpr int GEMV_NT = 8;          // tokens handled per pass of the GEMV kernels
 constexpr int ROUTE_KC = 256;       // K chunk of the router logits kernel (decode tiling)
 
+constexpr int W_MX = COLI_W_MXFP4;  // MXFP4 weights: 4-bit E2M1 codes, one E8M0 byte per 32 inputs
+
 // Packed bytes of one row of n inputs.
-__host__ __device__ inline int64_t row_bytes(int wfmt, int n) { return (int64_t)n * wfmt / 8; }
+__host__ __device__ inline int64_t row_bytes(int wfmt, int n) {
+  return wfmt == W_MX ? (int64_t)n / 2 : (int64_t)n * wfmt / 8;
+}
+
+// Group scales (one per GSZ<WB> inputs of a row): fp32, or E8M0 bytes for MXFP4.
+// gs_base gives element `elem` of the layer's scale array; gs_load reads element i
+// from there as fp32. E8M0 byte u is 2^(u - 127), u = 255 is NaN (OCP MX v1.0).
+template <int WB>
+constexpr int GSZ = (WB == W_MX) ? 32 : 64;
+
+template <int WB>
+__device__ __forceinline__ const void *gs_base(const float *scales, int64_t elem) {
+  if constexpr (WB == W_MX) return reinterpret_cast<const uint8_t *>(scales) + elem;
+  else return scales + elem;
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t u) {
+  return __uint_as_float(u == 0 ? 0x00400000u : (u == 255 ? 0x7fc00000u : u << 23));
+}
+
+template <int WB>
+__device__ __forceinline__ float gs_load(const void *base, int64_t i) {
+  if constexpr (WB == W_MX) return e8m0_f32(static_cast<const uint8_t *>(base)[i]);
+  else return static_cast<const float *>(base)[i];
+}
 
 struct WsLayout {
   // byte offsets into the workspace (all 256-byte aligned)

@@ -45,12 +45,14 @@ static int check_cfg(const coli_moe_cfg *c) {
   if (c->hidden <= 0 || c->ffn <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->n_group <= 0 ||
       c->topk_group <= 0)
     return COLI_E_INVALID;
-  if (c->wfmt != 2 && c->wfmt != 4 && c->wfmt != 8) return COLI_E_INVALID;
+  if (c->wfmt != 2 && c->wfmt != 4 && c->wfmt != 8 && c->wfmt != COLI_W_MXFP4) return COLI_E_INVALID;
   if (c->has_shared != 0 && c->has_shared != 1) return COLI_E_INVALID;
   if (c->n_experts % c->n_group || c->topk_group > c->n_group) return COLI_E_INVALID;
   if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return COLI_E_INVALID;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return COLI_E_INVALID;  // NaN
-  if (c->scale_group != 0 && c->scale_group != 64) return COLI_E_INVALID;
+  // MXFP4 carries one E8M0 scale per 32 inputs; the integer formats one per row or per 64
+  if (c->wfmt == COLI_W_MXFP4 ? c->scale_group != 32 : (c->scale_group != 0 && c->scale_group != 64))
+    return COLI_E_INVALID;
   if (!(c->topp >= 0.0f && c->topp <= 1.0f)) return COLI_E_INVALID;  // NaN included
   if (c->hidden % 128 || c->ffn % 128) return COLI_E_UNSUPPORTED;
   if (c->n_experts > 1024 || c->n_group > 64 || c->top_k > 64) return COLI_E_UNSUPPORTED;

@@ -54,6 +54,25 @@ struct Fmt<2> {
   static constexpr int BPC = 2;
   static constexpr float INV = 0.015625f;  // the top-bit bytes read 64 * w
 };
+template <>
+struct Fmt<W_MX> {
+  static constexpr int CHUNK = 16;         // one block of 32 E2M1 codes, int4 nibble order
+  static constexpr int BPC = 1;
+  static constexpr float INV = 0.5f;       // the table bytes read 2 * e2m1
+};
+
+// Four E2M1 codes, one in the low nibble of each byte of n (high nibbles ignored),
+// to four int8 bytes holding twice their values (integers in [-12, 12], so block
+// dots stay exact int32). One byte permute looks up the magnitude 2 * |v| of
+// codes 0..7, a second one its negation; the sign bit of each code selects.
+__device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t n) {
+  const uint32_t mag = n & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);  // 0 1 2 3 | 4 6 8 12
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);  // negated
+  const uint32_t sgn = (n >> 3) & 0x01010101u;
+  const uint32_t msk = (sgn << 8) - sgn;  // 0xFF in the bytes of negative codes
+  return (neg & msk) | (pos & ~msk);
+}
 
 __device__ __forceinline__ int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
 
@@ -73,6 +92,20 @@ __device__ __forceinline__ float chunk_dot<4>(const uint32_t (&wq)[4], const int
   for (int i = 0; i < 4; i++) {
     acc = dot4((int)((wq[i] << 4) & 0xF0F0F0F0u), xv[i], acc);
     acc = dot4((int)(wq[i] & 0xF0F0F0F0u), xv[4 + i], acc);
+  }
+  return xd[0] * (float)acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<W_MX>(const uint32_t (&wq)[4], const int8_t *xa, const float *xd) {
+  const int4 xl = *reinterpret_cast<const int4 *>(xa);
+  const int4 xh = *reinterpret_cast<const int4 *>(xa + 16);
+  const int xv[8] = {xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+  int acc = 0;  // 2 * J_b
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    acc = dot4((int)e2m1x4_to_i8x4(wq[i]), xv[i], acc);
+    acc = dot4((int)e2m1x4_to_i8x4(wq[i] >> 4), xv[4 + i], acc);
   }
   return xd[0] * (float)acc;
 }
@@ -143,6 +176,12 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK
   } else if constexpr (WB == 8) {
 #pragma unroll
     for (int i = 0; i < 8; i++) u[i] = (int)wq[i];
+  } else if constexpr (WB == W_MX) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      u[i] = (int)e2m1x4_to_i8x4(wq[i]);
+      u[4 + i] = (int)e2m1x4_to_i8x4(wq[i] >> 4);
+    }
   } else {
     // block blk, element dword d (elements 4d..4d+3) = field m of source dword h, d = 2m + h
 #pragma unroll
@@ -388,10 +427,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   const float *sc = a.scales + (int64_t)e * a.scale_stride;
   const float *sc0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * a.F;
   const float *sc1 = sc + a.F;
-  // group scales: gate [F][H/64] | up [F][H/64] | down [H][F/64]
-  const int64_t ngh = (int64_t)a.F * (a.H / 64);
-  const float *gsc0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * ngh;
-  const float *gsc1 = sc + ngh;
+  // group scales (G = GSZ inputs): gate [F][H/G] | up [F][H/G] | down [H][F/G]
+  constexpr int G = GSZ<WB>;
+  const int64_t ngh = (int64_t)a.F * (a.H / G);
+  const int64_t se = (int64_t)e * a.scale_stride;
+  const void *gsc0 = gs_base<WB>(a.scales, (MODE == MODE_GATEUP) ? se : se + 2 * ngh);
+  const void *gsc1 = gs_base<WB>(a.scales, se + ngh);
 
   extern __shared__ __align__(16) char smem[];
   int8_t *xs = reinterpret_cast<int8_t *>(smem);                      // [NT][K]
@@ -453,9 +494,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
         const int kx = c * BPC * QK;  // first input of this chunk
         float g0 = 1.0f, g1 = 1.0f;
         if constexpr (GS) {
-          const int64_t gi = (int64_t)r * (K / 64) + kx / 64;
-          g0 = gsc0[gi];
-          if constexpr (NMAT == 2) g1 = gsc1[gi];
+          const int64_t gi = (int64_t)r * (K / G) + kx / G;
+          g0 = gs_load<WB>(gsc0, gi);
+          if constexpr (NMAT == 2) g1 = gs_load<WB>(gsc1, gi);
         }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -546,7 +587,7 @@ struct FastCtx {
   const float *xds;  // LDS block scales [ntmax][nkb]
   float *obuf;       // LDS results [NMAT][8][TILE]
   int r0;            // first row of the tile
-  const float *gs0, *gs1;  // group scales [rows][K/64] of the two matrices (GS only)
+  const void *gs0, *gs1;  // group scales [rows][K/G] of the two matrices (GS only; see gs_base)
 };
 
 template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS>
@@ -576,7 +617,7 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
       int rw = b0 + j * RPI + rs;
       rw = rw < WR ? rw : WR - 1;
       roff[j] = (int64_t)(c.r0 + wv * WR + rw) * c.rb;
-      goff[j] = (int64_t)(c.r0 + wv * WR + rw) * (c.K / 64);
+      goff[j] = (int64_t)(c.r0 + wv * WR + rw) * (c.K / GSZ<WB>);
     }
     float acc[V];
 #pragma unroll
@@ -595,7 +636,8 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
 #pragma unroll
         for (int j = 0; j < BR; j++)
 #pragma unroll
-          for (int m = 0; m < NMAT; m++) gsr[j][m] = (m == 0 ? c.gs0 : c.gs1)[goff[j] + ch * BPC * QK / 64];
+          for (int m = 0; m < NMAT; m++)
+            gsr[j][m] = gs_load<WB>(m == 0 ? c.gs0 : c.gs1, goff[j] + ch * BPC * QK / GSZ<WB>);
       }
       Act<WB> act[NTC];
 #pragma unroll
@@ -666,9 +708,10 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   c.obuf = obuf;
   c.r0 = blockIdx.x * TILE;
   {
-    const int64_t ngh = (int64_t)a.F * (a.H / 64);
-    c.gs0 = (MODE == MODE_GATEUP) ? sc : sc + 2 * ngh;
-    c.gs1 = sc + ngh;
+    const int64_t ngh = (int64_t)a.F * (a.H / GSZ<WB>);
+    const int64_t se = (int64_t)e * a.scale_stride;
+    c.gs0 = gs_base<WB>(a.scales, (MODE == MODE_GATEUP) ? se : se + 2 * ngh);
+    c.gs1 = gs_base<WB>(a.scales, se + ngh);
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -989,15 +1032,16 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
       for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? mat0 : mat1) + roff + lane_w, w[j][m]);
     }
     if constexpr (GS) {
-      // group scales: gate [F][H/64] | up [F][H/64] | down [H][F/64]
-      const int64_t ngh = (int64_t)a.F * (a.H / 64);
-      const float *gsc = a.scales + (int64_t)e * a.scale_stride + ((MODE == MODE_GATEUP) ? 0 : 2 * ngh);
+      // group scales (G = GSZ inputs): gate [F][H/G] | up [F][H/G] | down [H][F/G]
+      constexpr int G = GSZ<WB>;
+      const int64_t ngh = (int64_t)a.F * (a.H / G);
+      const void *gsc = gs_base<WB>(a.scales, (int64_t)e * a.scale_stride + ((MODE == MODE_GATEUP) ? 0 : 2 * ngh));
 #pragma unroll
       for (int j = 0; j < R; j++) {
         if (h >= 0 && j / RH != h) continue;
-        const int64_t goff = (int64_t)(r0 + wvu * WR + j * RPI + rs) * (K / 64) + lane_x / 64;
+        const int64_t goff = (int64_t)(r0 + wvu * WR + j * RPI + rs) * (K / G) + lane_x / G;
 #pragma unroll
-        for (int m = 0; m < NMAT; m++) gsr[j][m] = gsc[m * ngh + goff];
+        for (int m = 0; m < NMAT; m++) gsr[j][m] = gs_load<WB>(gsc, m * ngh + goff);
       }
     }
   };
@@ -1314,6 +1358,8 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t launch_fmt(int wfmt, const FfnArgs &a, hipStream_t s) {
+  // MXFP4 always has its E8M0 scale per 32 inputs; the integer formats one per row or per 64
+  if (wfmt == W_MX) return a.gs == 32 ? launch_mode<W_MX, MODE, true>(a, s) : hipErrorInvalidValue;
   if (a.gs != 0 && a.gs != 64) return hipErrorInvalidValue;
   const bool gs = a.gs != 0;
   switch (wfmt) {

@@ -94,20 +94,33 @@ __global__ __launch_bounds__(1024) void plan_kernel(FfnArgs a, int4 *__restrict_
 // complement keeps the sign). One AND (and a shift) per four values, and the block
 // dots come out as exact multiples SCALE * I_b; the accumulated sums are divided
 // by SCALE at the end, exactly (a power of two).
+// MXFP4 codes go through a byte table instead: the byte holds 2 * e2m1 (SCALE 2).
 template <int WB>
 struct Top {
-  static constexpr int scale = (WB == 4) ? 16 : (WB == 2) ? 64 : 1;
+  static constexpr int scale = (WB == 4) ? 16 : (WB == 2) ? 64 : (WB == W_MX) ? 2 : 1;
+  static constexpr int block_bytes = (WB == W_MX) ? 16 : QK * WB / 8;  // packed bytes per block
 };
+
+// Four E2M1 codes (low nibbles of n's bytes) to int8 bytes 2 * e2m1: a byte permute
+// looks up 2|v| of the magnitude code, a second one -2|v|, the sign bit selects.
+__device__ __forceinline__ uint32_t mf_e2m1x4(uint32_t n) {
+  const uint32_t mag = n & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);
+  const uint32_t sgn = (n >> 3) & 0x01010101u;
+  const uint32_t msk = (sgn << 8) - sgn;
+  return (neg & msk) | (pos & ~msk);
+}
 
 // LDS tiles of one K stage of KC blocks, int8 in natural K order; rows padded by
 // 16 bytes against bank conflicts.
-template <int NMAT, int KC>
+template <int NMAT, int KC, int G>
 struct MfLds {
   static constexpr int ROWB = KC * QK + 16;  // bytes per row (and per token)
   int8_t a[2][NMAT][MF_ROWS][ROWB];
   int8_t b[2][MF_TOK][ROWB];
   float d[2][MF_TOK][KC];  // block scale of each token
-  __attribute__((aligned(16))) float gs[2][NMAT][KC * QK / 64][MF_ROWS];  // group scales of the stage's rows
+  __attribute__((aligned(16))) float gs[2][NMAT][KC * QK / G][MF_ROWS];  // group scales of the stage's rows
 };
 
 enum { MF_GATEUP = 0, MF_DOWN = 1 };
@@ -116,15 +129,16 @@ enum { MF_GATEUP = 0, MF_DOWN = 1 };
 // rows, of the token rows and of the block scales.
 template <int WB, int NMAT, int KC>
 struct MfRegs {
-  // weight bytes per (matrix, row) and stage: KC * 32 * WB / 8; 16-byte pieces per row
-  static constexpr int APIECES = KC * QK * WB / 8 / 16;
+  // weight bytes per (matrix, row) and stage: KC blocks; 16-byte pieces per row
+  static constexpr int APIECES = KC * Top<WB>::block_bytes / 16;
   static constexpr int ATOTAL = NMAT * MF_ROWS * APIECES;
   static constexpr int ALOADS = (ATOTAL + 255) / 256;  // per thread (the last may be partial)
   static constexpr int BLOADS = (MF_TOK * KC * QK / 16 + 255) / 256;
   uint4 a[ALOADS];
   uint4 b[BLOADS];
   float d;
-  float gs;
+  float gs;      // group scale (fp32 formats)
+  uint32_t gsx;  // MXFP4: the stage's KC = 4 E8M0 bytes of one row
 };
 
 // ------------------------------------------------------------------ GEMM
@@ -135,7 +149,7 @@ template <int WB, int MODE, int KC, bool GS>
 __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__restrict__ tiles,
                                                    const int32_t *__restrict__ ntiles, int gmax, int nf) {
   constexpr int NMAT = (MODE == MF_GATEUP) ? 2 : 1;
-  using Lds = MfLds<NMAT, KC>;
+  using Lds = MfLds<NMAT, KC, GSZ<WB>>;
   using Regs = MfRegs<WB, NMAT, KC>;
   constexpr int ROWB = Lds::ROWB;
   constexpr int APIECES = Regs::APIECES;
@@ -196,17 +210,21 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   }
   const bool dthread = tid < MF_TOK * KC;
   const int64_t doff = (int64_t)act_rows[dthread ? tid / KC : 0] * nkb + tid % KC;
-  // group scales of a stage: NMAT x (KC / 2) groups x 64 rows, one per thread;
-  // thread q -> matrix q / (NG * 64), group (q / 64) % NG, row q % 64
-  constexpr int NG = KC * QK / 64;
-  const bool gthread = GS && tid < NMAT * NG * MF_ROWS;
-  const float *gsrc = nullptr;
+  // group scales of a stage: NMAT x NG groups x 64 rows. fp32 (groups of 64): one per
+  // thread, thread q -> matrix q / (NG * 64), group (q / 64) % NG, row q % 64.
+  // MXFP4 (groups of 32): the row's KC = 4 E8M0 bytes as one 32-bit load per thread,
+  // thread q -> matrix q / 64, row q % 64 (K / 32 is a multiple of 4: aligned).
+  constexpr int G = GSZ<WB>;
+  constexpr int NG = KC * QK / G;
+  constexpr bool MXS = WB == W_MX;
+  static_assert(!MXS || KC == 4, "one 32-bit load holds a stage's four E8M0 bytes");
+  const bool gthread = GS && tid < NMAT * (MXS ? 1 : NG) * MF_ROWS;
+  const void *gsrc = nullptr;
   if constexpr (GS) {
-    const int sc_m = tid / (NG * MF_ROWS), sc_row = r0 + tid % MF_ROWS;
-    const int64_t ngh = (int64_t)a.F * (a.H / 64);
-    const float *base = a.scales + (int64_t)ti.x * a.scale_stride +
-                        ((MODE == MF_GATEUP) ? (sc_m == 1 ? ngh : 0) : 2 * ngh);
-    gsrc = base + (int64_t)sc_row * (K / 64) + (tid / MF_ROWS) % NG;
+    const int sc_m = tid / ((MXS ? 1 : NG) * MF_ROWS), sc_row = r0 + tid % MF_ROWS;
+    const int64_t ngh = (int64_t)a.F * (a.H / G);
+    const int64_t se = (int64_t)ti.x * a.scale_stride + ((MODE == MF_GATEUP) ? (sc_m == 1 ? ngh : 0) : 2 * ngh);
+    gsrc = gs_base<WB>(a.scales, se + (int64_t)sc_row * (K / G) + (MXS ? 0 : (tid / MF_ROWS) % NG));
   }
 
   auto gload = [&](int s, Regs &r) {
@@ -217,13 +235,18 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       if (ATOTAL % 256 != 0 && q >= ATOTAL) break;
       const int m = q / (MF_ROWS * APIECES), row = (q / APIECES) % MF_ROWS, pc = q % APIECES;
       const uint8_t *base = (NMAT == 2 && m == 1) ? mat1 : mat0;
-      r.a[j] = *reinterpret_cast<const uint4 *>(base + (int64_t)(r0 + row) * rb + (int64_t)kb0 * (QK * WB / 8) + pc * 16);
+      r.a[j] = *reinterpret_cast<const uint4 *>(base + (int64_t)(r0 + row) * rb + (int64_t)kb0 * Top<WB>::block_bytes +
+                                                pc * 16);
     }
 #pragma unroll
     for (int j = 0; j < Regs::BLOADS; j++)
       r.b[j] = *reinterpret_cast<const uint4 *>(asrc + boff[j] + (int64_t)kb0 * QK);
     if (dthread) r.d = dsrc[doff + kb0];
-    if (gthread) r.gs = gsrc[s * NG];
+    if constexpr (MXS) {
+      if (gthread) r.gsx = *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(gsrc) + s * KC);
+    } else {
+      if (gthread) r.gs = gs_load<WB>(gsrc, s * NG);
+    }
   };
 
   auto lstore = [&](int buf, const Regs &r) {
@@ -236,6 +259,19 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       const uint4 v = r.a[j];
       if constexpr (WB == 8) {
         *reinterpret_cast<uint4 *>(dst + pc * 16) = v;
+      } else if constexpr (WB == W_MX) {
+        // one block of 32 codes: 0..15 in the low nibbles, 16..31 in the high ones
+        uint4 lo, hi;
+        lo.x = mf_e2m1x4(v.x);
+        lo.y = mf_e2m1x4(v.y);
+        lo.z = mf_e2m1x4(v.z);
+        lo.w = mf_e2m1x4(v.w);
+        hi.x = mf_e2m1x4(v.x >> 4);
+        hi.y = mf_e2m1x4(v.y >> 4);
+        hi.z = mf_e2m1x4(v.z >> 4);
+        hi.w = mf_e2m1x4(v.w >> 4);
+        *reinterpret_cast<uint4 *>(dst + pc * 32) = lo;
+        *reinterpret_cast<uint4 *>(dst + pc * 32 + 16) = hi;
       } else if constexpr (WB == 4) {
         // one 16-byte block: values 0..15 in the low nibbles, 16..31 in the high ones
         uint4 lo, hi;
@@ -274,7 +310,14 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       *reinterpret_cast<uint4 *>(&L.b[buf][q / (2 * KC)][(q % (2 * KC)) * 16]) = r.b[j];
     }
     if (dthread) L.d[buf][tid / KC][tid % KC] = r.d;
-    if (gthread) L.gs[buf][tid / (NG * MF_ROWS)][(tid / MF_ROWS) % NG][tid % MF_ROWS] = r.gs;
+    if constexpr (MXS) {
+      if (gthread) {
+#pragma unroll
+        for (int kb = 0; kb < KC; kb++) L.gs[buf][tid / MF_ROWS][kb][tid % MF_ROWS] = e8m0_f32((r.gsx >> (8 * kb)) & 0xFFu);
+      }
+    } else {
+      if (gthread) L.gs[buf][tid / (NG * MF_ROWS)][(tid / MF_ROWS) % NG][tid % MF_ROWS] = r.gs;
+    }
   };
 
   float acc[NMAT][16];
@@ -297,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
         const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
         if constexpr (GS) {
           // rows wm * 32 + 8 q + 4 grp + (0..3) of the tile: four float4 reads
-          const float *gr = &L.gs[buf][m][kb * QK / 64][wm * 32 + 4 * grp];
+          const float *gr = &L.gs[buf][m][kb * QK / G][wm * 32 + 4 * grp];
 #pragma unroll
           for (int q = 0; q < 4; q++) {
             const float4 g4 = *reinterpret_cast<const float4 *>(gr + 8 * q);
@@ -431,7 +474,8 @@ static hipError_t launch_mf(const FfnArgs &a, const int4 *tiles, const int32_t *
   const int rows = (MODE == MF_GATEUP) ? a.F : a.H;
   const int K = (MODE == MF_GATEUP) ? a.H : a.F;
   if (rows % MF_ROWS || K % (MF_KC * QK) || gmax % 8) return hipErrorInvalidValue;
-  if (a.gs != 0 && a.gs != 64) return hipErrorInvalidValue;
+  // MXFP4 always has its E8M0 scale per 32 inputs; the integer formats one per row or per 64
+  if (WB == W_MX ? a.gs != 32 : (a.gs != 0 && a.gs != 64)) return hipErrorInvalidValue;
   const int nf = rows / MF_ROWS;
   const int64_t nwork = (int64_t)nf * gmax;
   if (nwork > 0x7fffffff) return hipErrorInvalidValue;
@@ -450,6 +494,7 @@ hipError_t launch_mfma_gateup(int wfmt, const FfnArgs &a, const int4 *tiles, con
     case 4: return launch_mf<4, MF_GATEUP>(a, tiles, ntiles, gmax, s);
     case 8: return launch_mf<8, MF_GATEUP>(a, tiles, ntiles, gmax, s);
     case 2: return launch_mf<2, MF_GATEUP>(a, tiles, ntiles, gmax, s);
+    case W_MX: return launch_mf<W_MX, MF_GATEUP>(a, tiles, ntiles, gmax, s);
   }
   return hipErrorInvalidValue;
 }
@@ -460,6 +505,7 @@ hipError_t launch_mfma_down(int wfmt, const FfnArgs &a, const int4 *tiles, const
     case 4: return launch_mf<4, MF_DOWN>(a, tiles, ntiles, gmax, s);
     case 8: return launch_mf<8, MF_DOWN>(a, tiles, ntiles, gmax, s);
     case 2: return launch_mf<2, MF_DOWN>(a, tiles, ntiles, gmax, s);
+    case W_MX: return launch_mf<W_MX, MF_DOWN>(a, tiles, ntiles, gmax, s);
   }
   return hipErrorInvalidValue;
 }

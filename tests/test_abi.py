@@ -38,6 +38,9 @@ def test_host_queries(q):
     assert q.blob_bytes(c) == 2 * 2048 * 3072 + 6144 * 1024
     assert q.blob_bytes(q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 8)) == 3 * 2048 * 6144
     assert q.blob_bytes(q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 2)) == 3 * 2048 * 6144 // 4
+    mx = q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, q.W_MXFP4, scale_group=32)
+    assert q.blob_bytes(mx) == 3 * 2048 * 6144 // 2
+    assert q.scales_per_expert(mx) == 3 * 2048 * 6144 // 32
     assert q.workspace_bytes(c, 16) > 0 and q.workspace_bytes(c, 2048) > q.workspace_bytes(c, 16)
     assert q.num_stages() == 7
     assert [q.stage_name(i) for i in range(7)][4] == "ffn_gate_up"
@@ -65,6 +68,8 @@ BAD_CFGS = [
     (dict(hidden=256, ffn=128, n_experts=2048, top_k=4), -2),                          # E > 1024
     (dict(hidden=16384, ffn=128, n_experts=16, top_k=4), -2),                          # LDS of the GEMV
     (dict(hidden=256, ffn=128, n_experts=16, top_k=4, scale_group=32), -1),            # group size 64 only
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, wbits=40), -1),                  # MXFP4: scale_group 32
+    (dict(hidden=256, ffn=128, n_experts=16, top_k=4, wbits=40, scale_group=64), -1),
     (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=1.5), -1),                  # topp in [0, 1]
     (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=-0.1), -1),
     (dict(hidden=256, ffn=128, n_experts=16, top_k=4, topp=float("nan")), -1),
