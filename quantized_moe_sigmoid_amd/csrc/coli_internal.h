@@ -44,6 +44,19 @@ __device__ __forceinline__ float gs_load(const void *base, int64_t i) {
   else return static_cast<const float *>(base)[i];
 }
 
+// Four E2M1 codes, one in the low nibble of each byte of n (high nibbles ignored),
+// to four int8 bytes holding twice their values (integers in [-12, 12], so block dots
+// stay exact int32). Byte permutes do the lookups: one returns 2|v| for the magnitude
+// bits, one -2|v|, and a third builds the per-byte select mask from the sign bit
+// (permute selectors 5 and 7 read a zero source byte, 13 and 15 give 0xFF).
+__device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t n) {
+  const uint32_t mag = n & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);  // 0 1 2 3 | 4 6 8 12
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);  // negated
+  const uint32_t msk = __builtin_amdgcn_perm(0u, 0u, (n & 0x08080808u) | 0x05050505u);
+  return (neg & msk) | (pos & ~msk);
+}
+
 struct WsLayout {
   // byte offsets into the workspace (all 256-byte aligned)
   size_t xq, xd, hq, hd, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, total;

@@ -61,18 +61,6 @@ struct Fmt<W_MX> {
   static constexpr float INV = 0.5f;       // the table bytes read 2 * e2m1
 };
 
-// Four E2M1 codes, one in the low nibble of each byte of n (high nibbles ignored),
-// to four int8 bytes holding twice their values (integers in [-12, 12], so block
-// dots stay exact int32). One byte permute looks up the magnitude 2 * |v| of
-// codes 0..7, a second one its negation; the sign bit of each code selects.
-__device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t n) {
-  const uint32_t mag = n & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);  // 0 1 2 3 | 4 6 8 12
-  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);  // negated
-  const uint32_t sgn = (n >> 3) & 0x01010101u;
-  const uint32_t msk = (sgn << 8) - sgn;  // 0xFF in the bytes of negative codes
-  return (neg & msk) | (pos & ~msk);
-}
 
 __device__ __forceinline__ int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
 

@@ -101,16 +101,6 @@ struct Top {
   static constexpr int block_bytes = (WB == W_MX) ? 16 : QK * WB / 8;  // packed bytes per block
 };
 
-// Four E2M1 codes (low nibbles of n's bytes) to int8 bytes 2 * e2m1: a byte permute
-// looks up 2|v| of the magnitude code, a second one -2|v|, the sign bit selects.
-__device__ __forceinline__ uint32_t mf_e2m1x4(uint32_t n) {
-  const uint32_t mag = n & 0x07070707u;
-  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, mag);
-  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, mag);
-  const uint32_t sgn = (n >> 3) & 0x01010101u;
-  const uint32_t msk = (sgn << 8) - sgn;
-  return (neg & msk) | (pos & ~msk);
-}
 
 // LDS tiles of one K stage of KC blocks, int8 in natural K order; rows padded by
 // 16 bytes against bank conflicts.
@@ -262,14 +252,14 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       } else if constexpr (WB == W_MX) {
         // one block of 32 codes: 0..15 in the low nibbles, 16..31 in the high ones
         uint4 lo, hi;
-        lo.x = mf_e2m1x4(v.x);
-        lo.y = mf_e2m1x4(v.y);
-        lo.z = mf_e2m1x4(v.z);
-        lo.w = mf_e2m1x4(v.w);
-        hi.x = mf_e2m1x4(v.x >> 4);
-        hi.y = mf_e2m1x4(v.y >> 4);
-        hi.z = mf_e2m1x4(v.z >> 4);
-        hi.w = mf_e2m1x4(v.w >> 4);
+        lo.x = e2m1x4_to_i8x4(v.x);
+        lo.y = e2m1x4_to_i8x4(v.y);
+        lo.z = e2m1x4_to_i8x4(v.z);
+        lo.w = e2m1x4_to_i8x4(v.w);
+        hi.x = e2m1x4_to_i8x4(v.x >> 4);
+        hi.y = e2m1x4_to_i8x4(v.y >> 4);
+        hi.z = e2m1x4_to_i8x4(v.z >> 4);
+        hi.w = e2m1x4_to_i8x4(v.w >> 4);
         *reinterpret_cast<uint4 *>(dst + pc * 32) = lo;
         *reinterpret_cast<uint4 *>(dst + pc * 32 + 16) = hi;
       } else if constexpr (WB == 4) {
