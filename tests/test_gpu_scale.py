@@ -29,11 +29,15 @@ def env():
     return q, oracle
 
 
-def _run(env, wl_index, T, sample, wbits=None, layer=0):
+def _run(env, wl_index, T, sample, wbits=None, layer=0, scale_group=0):
     import torch
     import synth.device
     q, orc = env
     wl = gu.workload_cfg(wl_index, wbits)
+    if wl["wbits"] == synth.W_MXFP4:
+        scale_group = 32
+    wl["scale_group"] = scale_group
+    print(f"full-size {wl['name']} wbits={wl['wbits']} scale_group={scale_group} T={T}", flush=True)
     seed = synth.workload_seed(wl_index, layer)
     H, F, E, S = wl["hidden"], wl["ffn"], wl["n_experts"], 1 if wl["has_shared"] else 0
     cfg = q.make_cfg(**wl)
@@ -42,7 +46,8 @@ def _run(env, wl_index, T, sample, wbits=None, layer=0):
     blobs = torch.empty((E + S) * blob, dtype=torch.uint8, device=d)
     synth.device.fill_blobs(blobs, seed, layer, 0, E + S, blob, wl["wbits"])
     inp = synth.layer_inputs(seed, layer, tokens=T, hidden=H, ffn=F, n_experts=E, has_shared=wl["has_shared"],
-                             wbits=wl["wbits"], zipf=wl.get("zipf", False), with_blobs=False)
+                             wbits=wl["wbits"], zipf=wl.get("zipf", False), with_blobs=False,
+                             scale_group=scale_group)
     w = q.Weights(blobs, gu.to_dev(inp["scales"]), gu.to_dev(inp["router_w"]), gu.to_dev(inp["router_bias"]))
     out, idx, tw = gu.run_layer(wl, w, inp["x"])
     ocfg = orc.make_cfg(**wl)
@@ -63,7 +68,7 @@ def _run(env, wl_index, T, sample, wbits=None, layer=0):
         got = blobs[e * blob:(e + 1) * blob].cpu().numpy()
         assert np.array_equal(got, synth.expert_blob(seed, layer, e, H, F, wl["wbits"]))
     sub = orc.make_cfg(hidden=H, ffn=F, n_experts=len(need), top_k=wl["top_k"], rsf=wl["rsf"],
-                       has_shared=wl["has_shared"], wbits=wl["wbits"])
+                       has_shared=wl["has_shared"], wbits=wl["wbits"], scale_group=scale_group)
     sidx = np.vectorize(remap.get)(ridx[toks]).astype(np.int32)
     ref = orc.ffn(sub, np.stack(hb), np.stack(hs), inp["x"][toks], sidx, rw[toks])
     err = gu.rel_err_per_token(out[toks], ref)
@@ -91,6 +96,20 @@ def test_glm_prefill_full_sampled(env):
 @pytest.mark.parametrize("wbits", [8, 2])
 def test_glm_verify_lowbit_full(env, wbits):
     _run(env, 4, 3, [0, 1, 2], wbits=wbits)
+
+
+@pytest.mark.parametrize("fmt", ["gs64", "mxfp4"])
+def test_decode_full_other_scale_formats(env, fmt):
+    """Group-scaled int4 and MXFP4 weights at the OLMoE and GLM decode sizes."""
+    kw = dict(scale_group=64) if fmt == "gs64" else dict(wbits=synth.W_MXFP4)
+    _run(env, 1, 16, range(16), **kw)
+    _run(env, 2, 16, [0, 8, 15], **kw)
+
+
+@pytest.mark.parametrize("fmt", ["gs64", "mxfp4"])
+def test_glm_prefill_full_sampled_other_scale_formats(env, fmt):
+    kw = dict(scale_group=64) if fmt == "gs64" else dict(wbits=synth.W_MXFP4)
+    _run(env, 3, 2048, [0, 1, 777, 2047], **kw)
 
 
 def test_graph_replay_matches_eager(env):
