@@ -134,3 +134,109 @@ def test_mxfp4_scales_reach_the_kernels(q, orc):
     rb, _, _ = orc.layer(orc.make_cfg(**cfgd), inp["blobs"], sc, inp["router_w"], inp["router_bias"], inp["x"])
     assert not np.array_equal(a, b)
     assert gu.rel_err_per_token(b, rb).max() <= TOL
+
+
+@pytest.mark.parametrize("T", [21, 150])
+def test_mxfp4_ffn_entry_vs_oracle(q, orc, T):
+    """coli_moe_ffn on the oracle's route (grouped by coli_moe_group) with MXFP4 weights
+    (T = 150: 750 pairs, the grouped-GEMM path)."""
+    import torch
+    cfgd = _cfg(hidden=384, ffn=512, n_experts=24, top_k=5, n_group=8, topk_group=3, rsf=2.5, has_shared=True)
+    inp = synth.layer_inputs(31, 0, tokens=T, hidden=384, ffn=512, n_experts=24, has_shared=True, wbits=MX,
+                             scale_group=32)
+    ocfg = orc.make_cfg(**cfgd)
+    ridx, rw = orc.route(ocfg, inp["router_w"], inp["router_bias"], inp["x"])
+    ref = orc.ffn(ocfg, inp["blobs"], inp["scales"], inp["x"], ridx, rw)
+    cfg = q.make_cfg(**cfgd)
+    d = gu.dev()
+    E, k = 24, 5
+    cnt = torch.empty(E, dtype=torch.int32, device=d)
+    off = torch.empty(E + 1, dtype=torch.int32, device=d)
+    perm = torch.empty(T * k, dtype=torch.int32, device=d)
+    act = torch.empty(E, dtype=torch.int32, device=d)
+    na = torch.empty(1, dtype=torch.int32, device=d)
+    idx_d = gu.to_dev(ridx)
+    q.group(cfg, idx_d, T, cnt, off, perm, act, na)
+    out = torch.empty((T, 384), dtype=torch.float32, device=d)
+    q.ffn(cfg, gu.upload_layer(inp), gu.to_dev(inp["x"]), idx_d, gu.to_dev(rw), off, perm, act, na, out,
+          q.alloc_workspace(cfg, T, d))
+    torch.cuda.synchronize()
+    assert gu.rel_err_per_token(out.cpu().numpy(), ref).max() <= TOL
+
+
+def test_mxfp4_empty_batch_is_a_noop(q):
+    """T = 0 with MXFP4 weights: the layer and FFN entry points succeed and write nothing."""
+    import torch
+    cfgd = _cfg(has_shared=True, n_group=2, topk_group=1)
+    cfg = q.make_cfg(**cfgd)
+    inp = synth.layer_inputs(5, 0, tokens=1, hidden=256, ffn=128, n_experts=16, has_shared=True, wbits=MX,
+                             scale_group=32)
+    w = gu.upload_layer(inp)
+    d = gu.dev()
+    x = torch.empty((0, 256), dtype=torch.float32, device=d)
+    out = torch.full((4, 256), float("nan"), dtype=torch.float32, device=d)
+    idx = torch.full((4, 4), -7, dtype=torch.int32, device=d)
+    tw = torch.full((4, 4), float("nan"), dtype=torch.float32, device=d)
+    ws = q.alloc_workspace(cfg, 1, d)
+    q.layer(cfg, w, x, out[:0], ws, idx[:0], tw[:0])
+    off = torch.full((17,), -7, dtype=torch.int32, device=d)
+    act = torch.full((16,), -7, dtype=torch.int32, device=d)
+    na = torch.full((1,), -7, dtype=torch.int32, device=d)
+    perm = torch.full((4,), -7, dtype=torch.int32, device=d)
+    q.ffn(cfg, w, x, idx[:0], tw[:0], off, perm[:0], act, na, out[:0], ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all() and torch.isnan(tw).all() and (idx == -7).all()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "gs64"])
+def test_deterministic_and_batch_invariant_other_scale_formats(q, fmt):
+    """Run to run bit-identical, and each token alone gives the bits it gets inside the
+    batch (OLMoE shape, decode path)."""
+    cfgd = _cfg(hidden=2048, ffn=1024, n_experts=64, top_k=8)
+    if fmt == "gs64":
+        cfgd.update(wbits=4, scale_group=64)
+    T = 16
+    inp = synth.layer_inputs(synth.workload_seed(1), 0, tokens=T, hidden=2048, ffn=1024, n_experts=64,
+                             has_shared=False, wbits=cfgd["wbits"], scale_group=cfgd["scale_group"])
+    w = gu.upload_layer(inp)
+    a = gu.run_layer(cfgd, w, inp["x"])
+    b = gu.run_layer(cfgd, w, inp["x"])
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    for t in (0, 7, 15):
+        s = gu.run_layer(cfgd, w, inp["x"][t:t + 1])
+        assert np.array_equal(s[0].view(np.uint32), a[0][t:t + 1].view(np.uint32))
+
+
+def test_mxfp4_graph_replay_matches_eager(q):
+    """A captured graph of MXFP4 layer calls (decode and grouped-GEMM sizes), replayed with
+    eager work and synchronisations in between, reproduces the eager results bit for bit."""
+    import torch
+    d = gu.dev()
+    runs = []
+    for cfgd, T in ((_cfg(hidden=2048, ffn=1024, n_experts=64, top_k=8), 4),
+                    (_cfg(hidden=512, ffn=512, n_experts=16, top_k=4, has_shared=True), 150)):
+        inp = synth.layer_inputs(7, 0, tokens=T, hidden=cfgd["hidden"], ffn=cfgd["ffn"],
+                                 n_experts=cfgd["n_experts"], has_shared=cfgd["has_shared"], wbits=MX,
+                                 scale_group=32)
+        cfg = q.make_cfg(**cfgd)
+        runs.append((cfg, gu.upload_layer(inp), gu.to_dev(inp["x"]),
+                     torch.empty((T, cfgd["hidden"]), dtype=torch.float32, device=d), q.alloc_workspace(cfg, T, d)))
+    eager = []
+    for cfg, w, x, out, ws in runs:
+        q.layer(cfg, w, x, out, ws)
+        eager.append(out.clone())
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(d)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for cfg, w, x, out, ws in runs:
+            q.layer(cfg, w, x, out, ws, stream=s)
+    for rep in range(3):
+        for r in runs:
+            r[3].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, r in enumerate(runs):
+            assert torch.equal(r[3].view(torch.int32), eager[i].view(torch.int32)), (rep, i)
+        _ = torch.randn(1000, device=d).sum().item()
