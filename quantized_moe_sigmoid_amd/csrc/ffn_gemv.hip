@@ -1309,8 +1309,9 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
       if (a.idx != nullptr)
         r = (lpr == 64) ? launch_pipe<WB, 64, MODE, GS>(a, NROWS, s) : launch_pipe<WB, 32, MODE, GS>(a, NROWS, s);
       // the register-resident kernel keeps one scale per row
-      if (r == hipErrorNotSupported && !GS)
-        r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
+      if constexpr (!GS)
+        if (r == hipErrorNotSupported)
+          r = (lpr == 64) ? launch_reg<WB, 64, MODE>(a, NROWS, slots, s) : launch_reg<WB, 32, MODE>(a, NROWS, slots, s);
       if (r != hipErrorNotSupported) return r;
     }
   }

@@ -469,10 +469,10 @@ static hipError_t launch_mf(const FfnArgs &a, const int4 *tiles, const int32_t *
   const int nf = rows / MF_ROWS;
   const int64_t nwork = (int64_t)nf * gmax;
   if (nwork > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.gs)
+  if (WB == W_MX || a.gs)  // MXFP4 always takes the group-scale path (a.gs == 32 checked above)
     hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC, true>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles,
                        gmax, nf);
-  else
+  else if constexpr (WB != W_MX)
     hipLaunchKernelGGL((mfma_kernel<WB, MODE, MF_KC, false>), dim3((unsigned)nwork), dim3(256), 0, s, a, tiles, ntiles,
                        gmax, nf);
   return hipGetLastError();
