@@ -112,6 +112,9 @@ LAYER_CASES = [  # cfg kwargs, T, seed
           topp=0.5), 131, 64),
     (_cfg(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, has_shared=True, wbits=8), 117, 65),
     (_cfg(hidden=512, ffn=256, n_experts=16, top_k=8, wbits=2, scale_group=64, topp=0.6), 90, 66),
+    # MXFP4 weights, decode and grouped-GEMM sizes
+    (_cfg(hidden=2048, ffn=1024, n_experts=64, top_k=8, wbits=40, scale_group=32), 16, 67),
+    (_cfg(hidden=512, ffn=1024, n_experts=16, top_k=8, wbits=40, scale_group=32, topp=0.6), 120, 68),
 ]
 
 
