@@ -195,6 +195,55 @@ const char *coli_moe_stage_name(int32_t stage);
 /* Static text for a status code. */
 const char *coli_moe_strerror(int status);
 
+/* ---- Expert residency tier: host RAM -> a pool of expert slots in HBM ----
+ * JustVugg/colibri README, "Never wait for the disk twice" and the I/O items: a per-layer
+ * LRU of experts with pinned ("hot") experts, missing experts loaded on demand, each expert
+ * of the batch union read once. Here the slow tier is host RAM and the fast tier a pool of
+ * `slots` expert blobs (+ scales) in HBM; the shared expert, when present, always lives in
+ * slot `slots` (the pool has slots + has_shared entries). The group/FFN entry points run on
+ * the pool unchanged, with cfg.n_experts = slots, the pool as coli_moe_weights.experts /
+ * .scales, and the route remapped to slot ids: the expert arithmetic, the pair order and
+ * the combine order are those of the resident layer, so the output is bit-identical to it.
+ * (Not built: loading the misses while the resident pairs compute, and the router lookahead
+ * one layer ahead.) */
+
+/* Host-side state of one layer's pool. All arrays are caller-owned host memory:
+ * slot_of [n_experts], expert_in [slots], last_use [slots], pinned [n_experts]. */
+typedef struct {
+  int32_t n_experts;  /* E */
+  int32_t slots;      /* HBM slots for routed experts, 1 <= slots <= E */
+  int32_t *slot_of;   /* slot holding expert e, or -1 */
+  int32_t *expert_in; /* expert held by slot s, or -1 */
+  uint64_t *last_use; /* LRU clock of the last batch that used slot s */
+  const uint8_t *pinned; /* 1: once loaded, never evicted (the pinned hot store); may be NULL */
+  uint64_t clock;     /* batches planned so far */
+} coli_tier;
+
+/* Empties the pool: slot_of = -1, expert_in = -1, last_use = 0, clock = 0.
+ * COLI_E_INVALID on NULL arrays or sizes out of range. */
+int coli_tier_init(coli_tier *t);
+
+/* Plans one batch. topk_idx (host, [T][k], expert ids or -1 for an empty slot) is the
+ * route; its distinct experts are the union. Experts of the union already in the pool are
+ * hits; each miss, in ascending expert order, takes an empty slot (lowest first) or evicts
+ * the least recently used slot whose expert is neither pinned nor in this union (lowest
+ * slot on ties). Outputs (host): slot_idx [T][k] = the route in slot ids (-1 kept);
+ * load_expert / load_slot [*n_load] = the misses and their slots (capacity: slots).
+ * COLI_E_INVALID for ids outside [-1, E); COLI_E_UNSUPPORTED when the union does not fit
+ * (more distinct experts than slots that can be freed). On error the state is unchanged. */
+int coli_tier_plan(coli_tier *t, const int32_t *topk_idx, int32_t T, int32_t k, int32_t *slot_idx,
+                   int32_t *load_expert, int32_t *load_slot, int32_t *n_load);
+
+/* Enqueues the host->HBM copies of a plan on `stream`: for each i, blob load_expert[i] of
+ * host_experts -> slot load_slot[i] of slot_experts, and its scales (coli_moe_scales_per_expert
+ * elements: fp32, or bytes for MXFP4) of host_scales -> slot_scales. load_expert may be E,
+ * the shared expert, with load_slot = slots. host_experts / host_scales should be pinned host
+ * memory (hipHostMalloc) for the copies to be asynchronous; they must stay valid until the
+ * stream has run them. slots: the pool's routed slot count. */
+int coli_moe_tier_stage(const coli_moe_cfg *cfg, int32_t slots, const void *host_experts, const void *host_scales,
+                        const int32_t *load_expert, const int32_t *load_slot, int32_t n_load, void *slot_experts,
+                        void *slot_scales, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,11 @@ EXPORTS = {
     "coli_moe_ffn": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                C.c_size_t, C.c_void_p]),
+    "coli_tier_init": (C.c_int, [C.c_void_p]),
+    "coli_tier_plan": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_void_p]),
+    "coli_moe_tier_stage": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "coli_moe_layer": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "coli_moe_layer_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
@@ -267,3 +272,51 @@ def layer_profiled(cfg: Cfg, w: Weights, x, out, workspace, events, stream=None)
     _check(lib().coli_moe_layer_profiled(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream, x), arr, len(handles)),
            "coli_moe_layer_profiled")
+
+
+# ------------------------------------------------------------------ expert tier
+class _TierC(C.Structure):
+    _fields_ = [("n_experts", C.c_int32), ("slots", C.c_int32), ("slot_of", C.c_void_p), ("expert_in", C.c_void_p),
+                ("last_use", C.c_void_p), ("pinned", C.c_void_p), ("clock", C.c_uint64)]
+
+
+class Tier:
+    """Host-side state of one layer's pool of `slots` HBM expert slots (coli_tier): which
+    expert each slot holds, LRU clocks, and the pinned experts (never evicted once loaded)."""
+
+    def __init__(self, n_experts: int, slots: int, pinned=None):
+        import numpy as np
+        self.slot_of = np.full(n_experts, -1, np.int32)
+        self.expert_in = np.full(slots, -1, np.int32)
+        self.last_use = np.zeros(slots, np.uint64)
+        self.pinned = None if pinned is None else np.ascontiguousarray(pinned, np.uint8)
+        self.c = _TierC(n_experts, slots, self.slot_of.ctypes.data, self.expert_in.ctypes.data,
+                        self.last_use.ctypes.data, None if self.pinned is None else self.pinned.ctypes.data, 0)
+        _check(lib().coli_tier_init(C.byref(self.c)), "coli_tier_init")
+
+    def plan(self, topk_idx):
+        """Plan one batch from a host route [T][k]: (slot_idx [T][k], load_expert, load_slot)."""
+        import numpy as np
+        idx = np.ascontiguousarray(topk_idx, np.int32)
+        T, k = idx.shape
+        slot_idx = np.empty_like(idx)
+        le = np.empty(self.c.slots, np.int32)
+        ls = np.empty(self.c.slots, np.int32)
+        n = C.c_int32(0)
+        _check(lib().coli_tier_plan(C.byref(self.c), idx.ctypes.data, T, k, slot_idx.ctypes.data, le.ctypes.data,
+                                    ls.ctypes.data, C.byref(n)), "coli_tier_plan")
+        return slot_idx, le[: n.value].copy(), ls[: n.value].copy()
+
+
+def tier_stage(cfg: Cfg, slots: int, host_experts, host_scales, load_expert, load_slot, slot_experts, slot_scales,
+               stream=None):
+    """Enqueue the host->HBM copies of a plan. host_*: CPU tensors (pinned for asynchronous
+    copies), slot_*: CUDA tensors of the pool; load_*: host int32 arrays."""
+    import numpy as np
+    le = np.ascontiguousarray(load_expert, np.int32)
+    ls = np.ascontiguousarray(load_slot, np.int32)
+    assert le.shape == ls.shape
+    _check(lib().coli_moe_tier_stage(C.byref(cfg), slots, C.c_void_p(host_experts.data_ptr()),
+                                     C.c_void_p(host_scales.data_ptr()), le.ctypes.data, ls.ctypes.data, le.size,
+                                     _ptr(slot_experts), _ptr(slot_scales), _stream(stream, slot_experts)),
+           "coli_moe_tier_stage")

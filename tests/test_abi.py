@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "coli_moe.h")
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(coli_moe_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(coli_(?:moe|tier)_\w+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,7 @@ def q():
 
 def test_exports_every_declared_symbol(q):
     names = _declared()
-    assert "coli_moe_layer" in names and "coli_moe_route" in names
+    assert "coli_moe_layer" in names and "coli_moe_route" in names and "coli_tier_plan" in names
     L = q.lib()
     for n in names:
         assert hasattr(L, n), n
