@@ -252,6 +252,141 @@ def copy_bandwidth(mbytes: int, reps: int):
     return 2 * n / dt / 1e9
 
 
+def h2d_bandwidth(mbytes: int = 256, reps: int = 5) -> float:
+    """Host->device copy rate from pinned host memory (GB/s): the practical PCIe peak
+    beside which the expert tier's copies are measured."""
+    import torch
+    n = mbytes << 20
+    src = torch.empty(n, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    return n * reps / (time.perf_counter() - t0) / 1e9
+
+
+def run_tier(args):
+    """The expert residency tier: every layer's experts in pinned host RAM, a pool of
+    `--tier-slots` HBM slots per layer managed by the LRU planner, misses copied host->HBM
+    inside the timed region. One step = one layer call on each of L stacked layers, with
+    route -> route to host -> plan -> stage misses -> group -> FFN on the pool; the inputs
+    cycle over 16 seeded batches per layer so that routes (and misses) change."""
+    import numpy as np
+    import torch
+    import quantized_moe_sigmoid_amd as q
+    import synth
+    import synth.device
+
+    wl = dict(synth.WORKLOADS[args.config])
+    if args.wbits is not None:
+        wl["wbits"] = args.wbits
+        if args.wbits == 40:
+            wl["scale_group"] = 32
+    if args.scale_group:
+        wl["scale_group"] = args.scale_group
+    T = int(args.tokens.split(",")[-1]) if args.tokens else wl["tokens"][-1]
+    E, H, slots, L = wl["n_experts"], wl["hidden"], args.tier_slots, args.layers
+    S = 1 if wl["has_shared"] else 0
+    if not 1 <= slots <= E:
+        raise SystemExit(f"--tier-slots must lie in 1..{E}")
+    cfg = q.make_cfg(**wl)
+    pcfg = q.make_cfg(**dict(wl, n_experts=slots, n_group=1, topk_group=1))
+    blob, nsc = q.blob_bytes(cfg), q.scales_per_expert(cfg)
+    d = torch.device("cuda:0")
+    h2d = h2d_bandwidth()
+    log(f"host->device copies from pinned memory: {h2d:.1f} GB/s")
+    layers = []
+    for l in range(L):
+        seed = synth.workload_seed(args.config, l)
+        tmp = torch.empty((E + S) * blob, dtype=torch.uint8, device=d)
+        synth.device.fill_blobs(tmp, seed, l, 0, E + S, blob, wl["wbits"])
+        hb = torch.empty((E + S) * blob, dtype=torch.uint8, pin_memory=True)
+        hb.copy_(tmp)
+        del tmp
+        inp = synth.layer_inputs(seed, l, tokens=1, hidden=H, ffn=wl["ffn"], n_experts=E, has_shared=wl["has_shared"],
+                                 wbits=wl["wbits"], zipf=wl.get("zipf", False), with_blobs=False,
+                                 scale_group=wl.get("scale_group", 0))
+        sc = np.ascontiguousarray(inp["scales"]).reshape(-1)
+        hs = torch.empty(sc.shape, dtype=torch.from_numpy(sc[:1]).dtype, pin_memory=True)
+        hs.copy_(torch.from_numpy(sc))
+        pool_b = torch.empty((slots + S) * blob, dtype=torch.uint8, device=d)
+        pool_s = torch.empty((slots + S) * nsc, dtype=hs.dtype, device=d)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+        rw, rb = up(inp["router_w"]), up(inp["router_bias"])
+        tier = q.Tier(E, slots)
+        if S:
+            q.tier_stage(cfg, slots, hb, hs, [E], [slots], pool_b, pool_s)
+        xs = [up(synth.activations(seed, l, T, H, index=100 + i)) for i in range(16)]
+        layers.append(dict(hb=hb, hs=hs, tier=tier, pool=q.Weights(pool_b, pool_s, rw, rb),
+                           resident=q.Weights(None, None, rw, rb), xs=xs))
+    ws = q.alloc_workspace(cfg, T, d)
+    pws = q.alloc_workspace(pcfg, T, d)
+    idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=d)
+    idx_h = torch.empty((T, cfg.top_k), dtype=torch.int32, pin_memory=True)
+    tw = torch.empty((T, cfg.top_k), dtype=torch.float32, device=d)
+    sidx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=d)
+    cnt = torch.empty(slots, dtype=torch.int32, device=d)
+    off = torch.empty(slots + 1, dtype=torch.int32, device=d)
+    perm = torch.empty(T * cfg.top_k, dtype=torch.int32, device=d)
+    act = torch.empty(slots, dtype=torch.int32, device=d)
+    na = torch.empty(1, dtype=torch.int32, device=d)
+    out = torch.empty((T, H), dtype=torch.float32, device=d)
+    stats = dict(loads=0, unions=0)
+
+    def layer_call(lay, step):
+        x = lay["xs"][step % 16]
+        q.route(cfg, lay["resident"], x, idx, tw, ws)
+        idx_h.copy_(idx)  # synchronous: the planner needs the route on the host
+        try:
+            slot_idx, le, ls = lay["tier"].plan(idx_h.numpy())
+        except q.ColiError as e:
+            raise SystemExit(f"the batch union does not fit in {slots} slots ({e}); use more --tier-slots")
+        q.tier_stage(cfg, slots, lay["hb"], lay["hs"], le, ls, lay["pool"].experts, lay["pool"].scales)
+        sidx.copy_(torch.from_numpy(slot_idx), non_blocking=False)
+        q.group(pcfg, sidx, T, cnt, off, perm, act, na)
+        q.ffn(pcfg, lay["pool"], x, sidx, tw, off, perm, act, na, out, pws)
+        stats["loads"] += le.size
+        stats["unions"] += len(set(slot_idx.ravel().tolist()) - {-1})
+
+    for w in range(args.warmup):
+        for lay in layers:
+            layer_call(lay, w)
+    torch.cuda.synchronize()
+    stats.update(loads=0, unions=0)
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        for lay in layers:
+            layer_call(lay, args.warmup + st)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    calls = args.steps * L
+    per_call = dt / calls
+    copy_bytes = stats["loads"] * (blob + nsc * (1 if wl["wbits"] == 40 else 4))
+    achieved = copy_bytes / dt / 1e9
+    hit = 1.0 - stats["loads"] / max(1, stats["unions"])
+    log(f"tier: {slots}/{E} slots, T={T}: {per_call * 1e6:.1f} us/layer call, {T / per_call:.0f} tok/s, "
+        f"hit rate {hit:.3f}, {stats['loads'] / calls:.1f} expert loads/call, copies {achieved:.1f} GB/s")
+    line = {
+        "metric": "MoE-layer tokens/s (decode, expert tier: host RAM -> HBM slots)",
+        "value": round(T / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_call * L * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8x" + {2: "int2", 4: "int4", 8: "int8", 40: "mxfp4"}[wl["wbits"]],
+        "data": "synthetic (seeded SplitMix64); experts in pinned host RAM, copies inside the timed region",
+        "config": {"workload": wl["name"] + "_tier", "tokens": T, "slots": slots, "n_experts": E,
+                   "stacked_layers": L, "scale_group": wl.get("scale_group", 0)},
+        "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": round(h2d, 2), "unit": "GB/s",
+                     "frac": round(achieved / h2d, 4), "traffic": None,
+                     "kernel": "host->HBM expert copies (hipMemcpyAsync)", "bytes_per_step": copy_bytes // args.steps},
+        "tier": {"hit_rate": round(hit, 4), "loads_per_call": round(stats["loads"] / calls, 2),
+                 "union_per_call": round(stats["unions"] / calls, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def gateup_ops(wl, T: int, pairs: float | None = None) -> int:
     """int8 multiply-add operations (x2) of one gate/up launch: every (token, expert)
     pair and every shared-expert row against 2F weight rows of H inputs."""
@@ -377,6 +512,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic summary and exit")
     ap.add_argument("--cmd", type=str, default="", help="the command that produced the profiler output")
+    ap.add_argument("--tier-slots", type=int, default=0,
+                    help="measure the expert tier instead: experts in pinned host RAM, this many HBM slots per layer")
     args = ap.parse_args()
 
     if args.summarize_stats:
@@ -390,6 +527,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's sharding across GPUs "
               "is a design note, not built", file=sys.stderr)
         sys.exit(2)
+
+    if args.tier_slots:
+        run_tier(args)
+        return
 
     import synth
     copy_gbs = None
