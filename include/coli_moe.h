@@ -204,8 +204,7 @@ const char *coli_moe_strerror(int status);
  * the pool unchanged, with cfg.n_experts = slots, the pool as coli_moe_weights.experts /
  * .scales, and the route remapped to slot ids: the expert arithmetic, the pair order and
  * the combine order are those of the resident layer, so the output is bit-identical to it.
- * (Not built: loading the misses while the resident pairs compute, and the router lookahead
- * one layer ahead.) */
+ * (Not built: the router lookahead one layer ahead.) */
 
 /* Host-side state of one layer's pool. All arrays are caller-owned host memory:
  * slot_of [n_experts], expert_in [slots], last_use [slots], pinned [n_experts]. */
@@ -243,6 +242,33 @@ int coli_tier_plan(coli_tier *t, const int32_t *topk_idx, int32_t T, int32_t k, 
 int coli_moe_tier_stage(const coli_moe_cfg *cfg, int32_t slots, const void *host_experts, const void *host_scales,
                         const int32_t *load_expert, const int32_t *load_slot, int32_t n_load, void *slot_experts,
                         void *slot_scales, void *stream);
+
+/* Workspace bytes of coli_moe_layer_tiered for up to T_max tokens on a pool of `slots`
+ * slots (0 if invalid). 256-byte aligned, like every workspace. */
+size_t coli_moe_tier_workspace_bytes(const coli_moe_cfg *cfg, int32_t slots, int32_t T_max);
+
+/* One layer through the tier, on `stream`, with the misses' loads overlapping the resident
+ * experts' compute (JustVugg/colibri README: missing experts load while resident ones
+ * compute):
+ *   1. route (w: router_w / router_bias; experts and scales unused) -> route to the host
+ *      (this call waits for `stream` here);
+ *   2. coli_tier_plan on *tier;
+ *   3. the misses are copied host->HBM on `copy_stream` (a second stream of the same device,
+ *      default priority) and `copy_event` is recorded after them;
+ *   4. the FFN of the pairs whose experts were resident runs on `stream` meanwhile;
+ *   5. `stream` waits for `copy_event`, then the FFN of the missing pairs and the combine
+ *      over every slot of every token run.
+ * The output is bit-identical to coli_moe_layer on the resident weights. The pool
+ * (pool_experts / pool_scales: slots + has_shared entries) must already hold the shared
+ * expert in slot `slots` (coli_moe_tier_stage with load_expert = E). host_experts /
+ * host_scales: all E + has_shared experts in pinned host memory. topk_idx_opt / topk_w_opt
+ * (device, [T][k]) receive the route (expert ids) when non-NULL. With no misses the whole
+ * FFN runs once, as in coli_moe_layer. COLI_E_UNSUPPORTED when the union does not fit
+ * (nothing is copied or computed after the route; *tier is unchanged). */
+int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
+                          const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
+                          const float *x, int32_t T, float *out, int32_t *topk_idx_opt, float *topk_w_opt,
+                          void *workspace, size_t ws_bytes, void *stream, void *copy_stream, void *copy_event);
 
 #ifdef __cplusplus
 }

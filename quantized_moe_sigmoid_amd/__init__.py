@@ -81,6 +81,10 @@ EXPORTS = {
                                  C.c_void_p]),
     "coli_moe_tier_stage": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "coli_moe_tier_workspace_bytes": (C.c_size_t, [C.c_void_p, C.c_int32, C.c_int32]),
+    "coli_moe_layer_tiered": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p]),
     "coli_moe_layer": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "coli_moe_layer_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
@@ -320,3 +324,48 @@ def tier_stage(cfg: Cfg, slots: int, host_experts, host_scales, load_expert, loa
                                      C.c_void_p(host_scales.data_ptr()), le.ctypes.data, ls.ctypes.data, le.size,
                                      _ptr(slot_experts), _ptr(slot_scales), _stream(stream, slot_experts)),
            "coli_moe_tier_stage")
+
+
+class HipEvent:
+    """A plain HIP event (timing disabled), e.g. the copy event of layer_tiered."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (the HIP runtime this process already uses)
+        self._hip = C.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self._hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.handle = C.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(C.byref(self.handle), 0x2)  # hipEventDisableTiming
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def close(self):
+        if self.handle:
+            self._hip.hipEventDestroy(self.handle)
+            self.handle = C.c_void_p()
+
+
+def tier_workspace_bytes(cfg: Cfg, slots: int, T_max: int) -> int:
+    return int(lib().coli_moe_tier_workspace_bytes(C.byref(cfg), slots, T_max))
+
+
+def alloc_tier_workspace(cfg: Cfg, slots: int, T_max: int, device):
+    import torch
+    n = tier_workspace_bytes(cfg, slots, T_max)
+    if n == 0:
+        raise ColiError(COLI_E_INVALID, "coli_moe_tier_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def layer_tiered(cfg: Cfg, w: Weights, tier: Tier, host_experts, host_scales, pool_experts, pool_scales, x, out,
+                 workspace, copy_stream, copy_event: HipEvent, topk_idx=None, topk_w=None, stream=None):
+    """coli_moe_layer_tiered: route, plan, misses copied on copy_stream while the resident
+    pairs compute on `stream`, then the missing pairs and the combine."""
+    import torch
+    _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out")
+    wc = w.c()
+    _check(lib().coli_moe_layer_tiered(C.byref(cfg), C.byref(wc), C.byref(tier.c), C.c_void_p(host_experts.data_ptr()),
+                                       C.c_void_p(host_scales.data_ptr()), _ptr(pool_experts), _ptr(pool_scales),
+                                       _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
+                                       workspace.numel(), _stream(stream, x), C.c_void_p(copy_stream.cuda_stream),
+                                       copy_event.handle), "coli_moe_layer_tiered")

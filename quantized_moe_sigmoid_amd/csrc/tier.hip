@@ -112,4 +112,125 @@ int coli_moe_tier_stage(const coli_moe_cfg *cfg, int32_t slots, const void *host
   return COLI_OK;
 }
 
+static coli_moe_cfg pool_cfg(const coli_moe_cfg &c, int32_t slots) {
+  coli_moe_cfg p = c;  // the FFN's view: `slots` experts, the router fields unused
+  p.n_experts = slots;
+  p.n_group = 1;
+  p.topk_group = 1;
+  p.topp = 0.0f;
+  return p;
+}
+
+static size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+namespace {
+struct TierWs {  // byte offsets of coli_moe_layer_tiered's workspace
+  size_t route, ffn, idx, w, sidx[2], cnt[2], off[2], perm[2], act[2], nact[2], total;
+};
+}  // namespace
+
+static bool tier_ws(const coli_moe_cfg *cfg, int32_t slots, int32_t T, TierWs &L) {
+  if (!cfg || slots <= 0 || slots > cfg->n_experts || cfg->top_k > slots) return false;
+  const coli_moe_cfg pc = pool_cfg(*cfg, slots);
+  const size_t a = coli_moe_workspace_bytes(cfg, T), b = coli_moe_workspace_bytes(&pc, T);
+  if (a == 0 || b == 0) return false;
+  const size_t P = (size_t)T * cfg->top_k, S = (size_t)slots;
+  size_t o = 0;
+  L.route = o;  o += a256(a);
+  L.ffn = o;    o += a256(b);
+  L.idx = o;    o += a256(P * 4);
+  L.w = o;      o += a256(P * 4);
+  for (int h = 0; h < 2; h++) {
+    L.sidx[h] = o; o += a256(P * 4);
+    L.cnt[h] = o;  o += a256(S * 4);
+    L.off[h] = o;  o += a256((S + 1) * 4);
+    L.perm[h] = o; o += a256(P * 4);
+    L.act[h] = o;  o += a256(S * 4);
+    L.nact[h] = o; o += 256;
+  }
+  L.total = o;
+  return true;
+}
+
+size_t coli_moe_tier_workspace_bytes(const coli_moe_cfg *cfg, int32_t slots, int32_t T_max) {
+  TierWs L;
+  if (T_max < 1 || !tier_ws(cfg, slots, T_max, L)) return 0;
+  return L.total;
+}
+
+int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
+                          const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
+                          const float *x, int32_t T, float *out, int32_t *topk_idx_opt, float *topk_w_opt,
+                          void *workspace, size_t ws_bytes, void *stream, void *copy_stream, void *copy_event) {
+  if (!cfg || !w || !tier || T < 0) return COLI_E_INVALID;
+  if (T == 0) return COLI_OK;
+  if (tier->n_experts != cfg->n_experts) return COLI_E_INVALID;
+  const int32_t slots = tier->slots, k = cfg->top_k;
+  TierWs L;
+  if (!tier_ws(cfg, slots, T, L)) return COLI_E_INVALID;
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return COLI_E_ALIGN;
+  if (!host_experts || !host_scales || !pool_experts || !pool_scales || !copy_stream || !copy_event)
+    return COLI_E_INVALID;
+  const coli_moe_cfg pc = pool_cfg(*cfg, slots);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  int32_t *idx = static_cast<int32_t *>(at(L.idx));
+  float *wt = static_cast<float *>(at(L.w));
+  hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+  const size_t P = (size_t)T * k;
+  const size_t a_bytes = L.ffn - L.route, b_bytes = L.idx - L.ffn;
+  int st;
+  // 1. route, and the route on the host
+  if ((st = coli_moe_route(cfg, w, x, T, idx, wt, at(L.route), a_bytes, stream))) return st;
+  std::vector<int32_t> hidx(P), hs(P), part[2] = {std::vector<int32_t>(P), std::vector<int32_t>(P)};
+  if (hipMemcpyAsync(hidx.data(), idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;
+  // 2. plan
+  std::vector<int32_t> le(slots), ls(slots);
+  int32_t nl = 0;
+  if ((st = coli_tier_plan(tier, hidx.data(), T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
+  // the two halves of the route in slot ids: resident pairs, then the missing pairs
+  std::vector<uint8_t> missing(slots, 0);
+  for (int32_t i = 0; i < nl; i++) missing[ls[i]] = 1;
+  for (size_t p = 0; p < P; p++) {
+    const int32_t v = hs[p];
+    const bool m = v >= 0 && missing[v];
+    part[0][p] = m ? -1 : v;
+    part[1][p] = m ? v : -1;
+  }
+  const int nphase = nl > 0 ? 2 : 1;
+  if (nl == 0) part[0] = hs;
+  for (int h = 0; h < nphase; h++)
+    if (hipMemcpyAsync(at(L.sidx[h]), part[h].data(), P * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+      return COLI_E_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;  // host vectors go out of scope
+  // 3. the misses' copies on the copy stream
+  if (nl > 0) {
+    if ((st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl, pool_experts,
+                                  pool_scales, copy_stream)))
+      return st;
+    if (hipEventRecord(static_cast<hipEvent_t>(copy_event), cs) != hipSuccess) return COLI_E_DEVICE;
+  }
+  const coli_moe_weights pw{pool_experts, static_cast<const float *>(pool_scales), w->router_w, w->router_bias};
+  for (int h = 0; h < nphase; h++) {
+    // 5. the missing pairs wait for their copies
+    if (h == 1 && hipStreamWaitEvent(s, static_cast<hipEvent_t>(copy_event), 0) != hipSuccess) return COLI_E_DEVICE;
+    const int32_t *si = static_cast<const int32_t *>(at(L.sidx[h]));
+    int32_t *cnt = static_cast<int32_t *>(at(L.cnt[h])), *off = static_cast<int32_t *>(at(L.off[h]));
+    int32_t *perm = static_cast<int32_t *>(at(L.perm[h])), *act = static_cast<int32_t *>(at(L.act[h]));
+    int32_t *nact = static_cast<int32_t *>(at(L.nact[h]));
+    if ((st = coli_moe_group(&pc, si, T, cnt, off, perm, act, nact, stream))) return st;
+    // 4./5. the FFN of this half; its ypair rows stay in the shared FFN workspace, and the
+    // last half's combine sums every slot (the weights of the whole route)
+    if ((st = coli_moe_ffn(&pc, &pw, x, T, si, wt, off, perm, act, nact, out, at(L.ffn), b_bytes, stream)))
+      return st;
+  }
+  if (topk_idx_opt && hipMemcpyAsync(topk_idx_opt, idx, P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return COLI_E_DEVICE;
+  if (topk_w_opt && hipMemcpyAsync(topk_w_opt, wt, P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return COLI_E_DEVICE;
+  return COLI_OK;
+}
+
 }  // extern "C"

@@ -96,3 +96,49 @@ def test_tiered_grouped_gemm_bitidentical_to_resident(q):
                synth.activations(61, 0, 160, 512, index=2)]
     tier, _ = _tiered_run(q, cfgd, 24, batches, 61)
     assert not np.array_equal(tier.expert_in, np.arange(24))  # not the identity placement
+
+
+@pytest.mark.parametrize("wbits,sg,Ts,slots", [(4, 0, (3,) * 6, 14), (40, 32, (3,) * 6, 14),
+                                               (4, 0, (3, 150, 3, 150, 160, 5), 36)])
+def test_layer_tiered_overlapped_bitidentical(q, wbits, sg, Ts, slots):
+    """coli_moe_layer_tiered: the misses copy on a second stream while the resident pairs
+    compute; batch after batch the output and the route equal the resident layer's, bit
+    for bit (T >= 150: grouped GEMMs, after small batches that leave part of the union
+    resident)."""
+    import torch
+    d = gu.dev()
+    T = max(Ts)
+    E = 32 if T < 100 else 36
+    cfgd = dict(hidden=512, ffn=256, n_experts=E, top_k=4, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
+                wbits=wbits, scale_group=sg)
+    seed = 700 + wbits + T
+    inp = synth.layer_inputs(seed, 0, tokens=1, hidden=512, ffn=256, n_experts=E, has_shared=True, wbits=wbits,
+                             scale_group=sg)
+    cfg = q.make_cfg(**cfgd)
+    blob, nsc = q.blob_bytes(cfg), q.scales_per_expert(cfg)
+    resident = gu.upload_layer(inp)
+    hb = torch.from_numpy(np.ascontiguousarray(inp["blobs"]).reshape(-1)).pin_memory()
+    hs = torch.from_numpy(np.ascontiguousarray(inp["scales"]).reshape(-1)).pin_memory()
+    pool_b = torch.zeros((slots + 1) * blob, dtype=torch.uint8, device=d)
+    pool_s = torch.zeros((slots + 1) * nsc, dtype=hs.dtype, device=d)
+    tier = q.Tier(E, slots)
+    q.tier_stage(cfg, slots, hb, hs, [E], [slots], pool_b, pool_s)
+    cs = torch.cuda.Stream(d)
+    ev = q.HipEvent()
+    ws = q.alloc_tier_workspace(cfg, slots, T, d)
+    loads_before = 0
+    for bi, T in enumerate(Ts):
+        print(f"tiered layer batch {bi} T={T} slots={slots} wbits={wbits}", flush=True)
+        x_np = synth.activations(seed, 0, T, 512, index=bi)
+        x = gu.to_dev(x_np)
+        out = torch.full((T, 512), float("nan"), dtype=torch.float32, device=d)
+        idx = torch.empty((T, 4), dtype=torch.int32, device=d)
+        tw = torch.empty((T, 4), dtype=torch.float32, device=d)
+        q.layer_tiered(cfg, resident, tier, hb, hs, pool_b, pool_s, x, out, ws, cs, ev, idx, tw)
+        ref, ridx, rw = gu.run_layer(cfgd, resident, x_np)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert np.array_equal(tw.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), bi
+    assert int(tier.c.clock) == len(Ts)
+    ev.close()
