@@ -132,3 +132,28 @@ def test_stage_rejects_bad_plans_before_copying(q):
     ls2 = (C.c_int32 * 2)(4, 4)  # routed expert into the shared slot
     assert L.coli_moe_tier_stage(C.byref(cfg), 4, p, p, le, ls2, 2, p, p, None) == qq.COLI_E_INVALID
     assert L.coli_moe_tier_stage(C.byref(cfg), 4, p, p, le, ls, 0, p, p, None) == qq.COLI_OK  # nothing to copy
+
+
+def test_tiered_entry_points_reject_bad_arguments_on_the_host(q):
+    """No GPU call is reached: every check happens before anything is enqueued."""
+    import ctypes as C
+    import quantized_moe_sigmoid_amd as qq
+    cfg = q.make_cfg(256, 128, 16, 4, has_shared=True)
+    L = q.lib()
+    assert L.coli_moe_tier_workspace_bytes(C.byref(cfg), 8, 16) > 0
+    assert L.coli_moe_tier_workspace_bytes(C.byref(cfg), 0, 16) == 0     # no slots
+    assert L.coli_moe_tier_workspace_bytes(C.byref(cfg), 17, 16) == 0    # more slots than experts
+    assert L.coli_moe_tier_workspace_bytes(C.byref(cfg), 3, 16) == 0     # k = 4 > slots
+    t = q.Tier(16, 8)
+    p = C.c_void_p(0x1000)
+    w = q.Weights(None, None, None, None).c()
+    args = lambda tier, T, ws_bytes: (C.byref(cfg), C.byref(w), tier, p, p, p, p, p, T, p, None, None, p, ws_bytes,
+                                      None, p, p)
+    fn = L.coli_moe_layer_tiered
+    assert fn(*args(None, 4, 1 << 30)) == qq.COLI_E_INVALID                # no tier state
+    assert fn(*args(C.byref(t.c), 0, 0)) == qq.COLI_OK                      # T = 0 is a no-op
+    assert fn(*args(C.byref(t.c), -1, 1 << 30)) == qq.COLI_E_INVALID
+    assert fn(*args(C.byref(t.c), 4, 16)) == qq.COLI_E_WORKSPACE            # workspace too small
+    t2 = q.Tier(12, 8)
+    assert fn(*args(C.byref(t2.c), 4, 1 << 30)) == qq.COLI_E_INVALID        # tier of another layer shape
+    assert int(t.c.clock) == 0
