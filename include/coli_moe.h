@@ -204,7 +204,7 @@ const char *coli_moe_strerror(int status);
  * the pool unchanged, with cfg.n_experts = slots, the pool as coli_moe_weights.experts /
  * .scales, and the route remapped to slot ids: the expert arithmetic, the pair order and
  * the combine order are those of the resident layer, so the output is bit-identical to it.
- * (Not built: the router lookahead one layer ahead.) */
+ * The router lookahead (coli_moe_tier_prefetch) stages a layer's predicted union ahead. */
 
 /* Host-side state of one layer's pool. All arrays are caller-owned host memory:
  * slot_of [n_experts], expert_in [slots], last_use [slots], pinned [n_experts]. */
@@ -269,6 +269,20 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
                           const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
                           const float *x, int32_t T, float *out, int32_t *topk_idx_opt, float *topk_w_opt,
                           void *workspace, size_t ws_bytes, void *stream, void *copy_stream, void *copy_event);
+
+/* Router lookahead (JustVugg/colibri README: a router-lookahead thread prefetches the next
+ * layer's experts; routing is largely predictable one layer ahead): routes x with the router
+ * of another layer (w: its router_w / router_bias; typically layer l+1's, applied to layer
+ * l's input), plans that union on that layer's *tier and enqueues the misses' copies into
+ * that layer's pool on copy_stream, then returns. The layer's next coli_moe_layer_tiered
+ * call on the same copy_stream waits for these copies before it reads the pool. Waits for
+ * `stream` after the route. workspace: coli_moe_tier_workspace_bytes(cfg, tier->slots, T).
+ * *n_loaded_opt receives the number of experts copied. COLI_E_UNSUPPORTED when the
+ * predicted union does not fit (nothing copied, *tier unchanged). */
+int coli_moe_tier_prefetch(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
+                           const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
+                           const float *x, int32_t T, void *workspace, size_t ws_bytes, void *stream,
+                           void *copy_stream, int32_t *n_loaded_opt);
 
 #ifdef __cplusplus
 }

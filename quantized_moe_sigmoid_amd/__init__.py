@@ -85,6 +85,9 @@ EXPORTS = {
     "coli_moe_layer_tiered": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "coli_moe_tier_prefetch": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p,
+                                         C.c_void_p, C.c_void_p]),
     "coli_moe_layer": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "coli_moe_layer_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
@@ -369,3 +372,18 @@ def layer_tiered(cfg: Cfg, w: Weights, tier: Tier, host_experts, host_scales, po
                                        _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
                                        workspace.numel(), _stream(stream, x), C.c_void_p(copy_stream.cuda_stream),
                                        copy_event.handle), "coli_moe_layer_tiered")
+
+
+def tier_prefetch(cfg: Cfg, w: Weights, tier: Tier, host_experts, host_scales, pool_experts, pool_scales, x,
+                  workspace, copy_stream, stream=None) -> int:
+    """coli_moe_tier_prefetch: stage the union that w's router predicts for x into that
+    layer's pool on copy_stream; returns the number of experts copied."""
+    import torch
+    _dt(x, torch.float32, "x")
+    wc = w.c()
+    n = C.c_int32(0)
+    _check(lib().coli_moe_tier_prefetch(C.byref(cfg), C.byref(wc), C.byref(tier.c), C.c_void_p(host_experts.data_ptr()),
+                                        C.c_void_p(host_scales.data_ptr()), _ptr(pool_experts), _ptr(pool_scales),
+                                        _ptr(x), x.shape[0], _ptr(workspace), workspace.numel(), _stream(stream, x),
+                                        C.c_void_p(copy_stream.cuda_stream), C.byref(n)), "coli_moe_tier_prefetch")
+    return n.value

@@ -205,7 +205,13 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
     if (hipMemcpyAsync(at(L.sidx[h]), part[h].data(), P * 4, hipMemcpyHostToDevice, s) != hipSuccess)
       return COLI_E_DEVICE;
   if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;  // host vectors go out of scope
-  // 3. the misses' copies on the copy stream
+  // 3. copies already enqueued on the copy stream (a lookahead prefetch into this pool: the
+  // planner counts their experts as resident) are waited for before the first half; the
+  // wait takes the event as recorded here, before this call's own copies are enqueued
+  hipEvent_t ev = static_cast<hipEvent_t>(copy_event);
+  if (hipEventRecord(ev, cs) != hipSuccess) return COLI_E_DEVICE;
+  if (hipStreamWaitEvent(s, ev, 0) != hipSuccess) return COLI_E_DEVICE;
+  // the misses' copies, and the event the missing pairs wait for
   if (nl > 0) {
     if ((st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl, pool_experts,
                                   pool_scales, copy_stream)))
@@ -230,6 +236,39 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
     return COLI_E_DEVICE;
   if (topk_w_opt && hipMemcpyAsync(topk_w_opt, wt, P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return COLI_E_DEVICE;
+  return COLI_OK;
+}
+
+int coli_moe_tier_prefetch(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
+                           const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
+                           const float *x, int32_t T, void *workspace, size_t ws_bytes, void *stream,
+                           void *copy_stream, int32_t *n_loaded_opt) {
+  if (n_loaded_opt) *n_loaded_opt = 0;
+  if (!cfg || !w || !tier || T < 0) return COLI_E_INVALID;
+  if (T == 0) return COLI_OK;
+  if (tier->n_experts != cfg->n_experts) return COLI_E_INVALID;
+  const int32_t slots = tier->slots, k = cfg->top_k;
+  TierWs L;
+  if (!tier_ws(cfg, slots, T, L)) return COLI_E_INVALID;
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return COLI_E_ALIGN;
+  if (!host_experts || !host_scales || !pool_experts || !pool_scales || !copy_stream) return COLI_E_INVALID;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  int32_t *idx = reinterpret_cast<int32_t *>(ws + L.idx);
+  float *wt = reinterpret_cast<float *>(ws + L.w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t P = (size_t)T * k;
+  int st;
+  if ((st = coli_moe_route(cfg, w, x, T, idx, wt, ws + L.route, L.ffn - L.route, stream))) return st;
+  std::vector<int32_t> hidx(P), hs(P), le(slots), ls(slots);
+  if (hipMemcpyAsync(hidx.data(), idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;
+  int32_t nl = 0;
+  if ((st = coli_tier_plan(tier, hidx.data(), T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
+  if (nl > 0 && (st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl,
+                                          pool_experts, pool_scales, copy_stream)))
+    return st;
+  if (n_loaded_opt) *n_loaded_opt = nl;
   return COLI_OK;
 }
 

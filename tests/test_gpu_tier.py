@@ -142,3 +142,55 @@ def test_layer_tiered_overlapped_bitidentical(q, wbits, sg, Ts, slots):
         assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), bi
     assert int(tier.c.clock) == len(Ts)
     ev.close()
+
+
+def test_router_lookahead_prefetch_then_layer_bitidentical(q):
+    """Layer B's router applied to layer A's input stages B's predicted union while A runs;
+    B's tiered call (its input A's plus a small residual update) waits for those copies and
+    equals the resident layer B bit for bit. The prefetch must cover part of B's union."""
+    import torch
+    d = gu.dev()
+    E, slots, T = 32, 14, 3
+    cfgd = dict(hidden=512, ffn=256, n_experts=E, top_k=4, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
+                wbits=4, scale_group=0)
+    cfg = q.make_cfg(**cfgd)
+    blob, nsc = q.blob_bytes(cfg), q.scales_per_expert(cfg)
+    lay = []
+    for l in range(2):
+        inp = synth.layer_inputs(800 + l, 0, tokens=1, hidden=512, ffn=256, n_experts=E, has_shared=True, wbits=4)
+        hb = torch.from_numpy(np.ascontiguousarray(inp["blobs"]).reshape(-1)).pin_memory()
+        hs = torch.from_numpy(np.ascontiguousarray(inp["scales"]).reshape(-1)).pin_memory()
+        pb = torch.zeros((slots + 1) * blob, dtype=torch.uint8, device=d)
+        ps = torch.zeros((slots + 1) * nsc, dtype=torch.float32, device=d)
+        tier = q.Tier(E, slots)
+        q.tier_stage(cfg, slots, hb, hs, [E], [slots], pb, ps)
+        lay.append(dict(res=gu.upload_layer(inp), hb=hb, hs=hs, pb=pb, ps=ps, tier=tier))
+    cs = torch.cuda.Stream(d)
+    ev = q.HipEvent()
+    ws = q.alloc_tier_workspace(cfg, slots, T, d)
+    prefetched, later_loads = 0, 0
+    for bi in range(6):
+        print(f"lookahead batch {bi}", flush=True)
+        xa_np = synth.activations(810, 0, T, 512, index=bi)
+        xb_np = (xa_np + 0.3 * synth.activations(811, 0, T, 512, index=bi)).astype(np.float32)
+        xa, xb = gu.to_dev(xa_np), gu.to_dev(xb_np)
+        outs = []
+        for l, x in ((0, xa), (1, xb)):
+            L = lay[l]
+            if l == 1:
+                before = L["tier"].slot_of.copy()
+            out = torch.full((T, 512), float("nan"), dtype=torch.float32, device=d)
+            q.layer_tiered(cfg, L["res"], L["tier"], L["hb"], L["hs"], L["pb"], L["ps"], x, out, ws, cs, ev)
+            if l == 1:
+                later_loads += int(((L["tier"].slot_of >= 0) & (before < 0)).sum())
+            outs.append(out)
+            if l == 0:  # lookahead: B's router on A's input, staged while A's work drains
+                prefetched += q.tier_prefetch(cfg, lay[1]["res"], lay[1]["tier"], lay[1]["hb"], lay[1]["hs"],
+                                              lay[1]["pb"], lay[1]["ps"], xa, ws, cs)
+        for l, x_np in ((0, xa_np), (1, xb_np)):
+            ref, _, _ = gu.run_layer(cfgd, lay[l]["res"], x_np)
+            torch.cuda.synchronize()
+            assert np.array_equal(outs[l].cpu().numpy().view(np.uint32), ref.view(np.uint32)), (bi, l)
+    ev.close()
+    assert prefetched > 0
+    print(f"prefetched {prefetched} experts, {later_loads} loaded on demand", flush=True)
