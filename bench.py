@@ -320,16 +320,28 @@ def run_tier(args):
         tier = q.Tier(E, slots)
         if S:
             q.tier_stage(cfg, slots, hb, hs, [E], [slots], pool_b, pool_s)
-        xs = [up(synth.activations(seed, l, T, H, index=100 + i)) for i in range(16)]
+        if args.tier_residual > 0:
+            # a synthetic residual stream: layer l's input is layer l-1's plus sigma * noise
+            seed0 = synth.workload_seed(args.config, 0)
+            xs = []
+            for i in range(16):
+                xv = synth.activations(seed0, 0, T, H, index=100 + i)
+                for j in range(1, l + 1):
+                    xv = xv + args.tier_residual * synth.activations(seed0, j, T, H, index=200 + i)
+                xs.append(up(xv.astype(np.float32)))
+        else:
+            xs = [up(synth.activations(seed, l, T, H, index=100 + i)) for i in range(16)]
         layers.append(dict(hb=hb, hs=hs, tier=tier, pool=q.Weights(pool_b, pool_s, rw, rb),
                            resident=q.Weights(None, None, rw, rb), xs=xs))
     tws = q.alloc_tier_workspace(cfg, slots, T, d)
+    pfws = q.alloc_tier_workspace(cfg, slots, T, d)  # the lookahead's own route scratch
+    rs = torch.cuda.Stream(d)                          # the lookahead's router stream
     out = torch.empty((T, H), dtype=torch.float32, device=d)
     cs = torch.cuda.Stream(d)
     ev = q.HipEvent()
-    stats = dict(loads=0, unions=0)
+    stats = dict(loads=0, unions=0, prefetched=0)
 
-    def layer_call(lay, step):
+    def layer_call(lay, step, nxt=None):
         x = lay["xs"][step % 16]
         tier = lay["tier"]
         prev = tier.slot_of.copy()
@@ -340,25 +352,35 @@ def run_tier(args):
             raise SystemExit(f"the batch union does not fit in {slots} slots ({e}); use more --tier-slots")
         stats["loads"] += int(((tier.slot_of >= 0) & (prev < 0)).sum())      # experts copied in this call
         stats["unions"] += int((tier.last_use == tier.c.clock).sum())        # slots this batch used
+        if nxt is not None:  # lookahead: the next layer's router on this layer's input, on its own stream
+            try:
+                stats["prefetched"] += q.tier_prefetch(cfg, nxt["pool"], nxt["tier"], nxt["hb"], nxt["hs"],
+                                                       nxt["pool"].experts, nxt["pool"].scales, x, pfws, cs, stream=rs)
+            except q.ColiError:
+                pass  # a predicted union that does not fit is not prefetched
+
+    def step_all(st):
+        for li, lay in enumerate(layers):
+            nxt = layers[li + 1] if args.tier_lookahead and li + 1 < L else None
+            layer_call(lay, st, nxt)
 
     for w in range(args.warmup):
-        for lay in layers:
-            layer_call(lay, w)
+        step_all(w)
     torch.cuda.synchronize()
-    stats.update(loads=0, unions=0)
+    stats.update(loads=0, unions=0, prefetched=0)
     t0 = time.perf_counter()
     for st in range(args.steps):
-        for lay in layers:
-            layer_call(lay, args.warmup + st)
+        step_all(args.warmup + st)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     calls = args.steps * L
     per_call = dt / calls
-    copy_bytes = stats["loads"] * (blob + nsc * (1 if wl["wbits"] == 40 else 4))
+    copy_bytes = (stats["loads"] + stats["prefetched"]) * (blob + nsc * (1 if wl["wbits"] == 40 else 4))
     achieved = copy_bytes / dt / 1e9
     hit = 1.0 - stats["loads"] / max(1, stats["unions"])
     log(f"tier: {slots}/{E} slots, T={T}: {per_call * 1e6:.1f} us/layer call, {T / per_call:.0f} tok/s, "
-        f"hit rate {hit:.3f}, {stats['loads'] / calls:.1f} expert loads/call, copies {achieved:.1f} GB/s")
+        f"hit rate {hit:.3f}, {stats['loads'] / calls:.1f} expert loads/call on demand, "
+        f"{stats['prefetched'] / calls:.1f} prefetched/call, copies {achieved:.1f} GB/s")
     line = {
         "metric": "MoE-layer tokens/s (decode, expert tier: host RAM -> HBM slots)",
         "value": round(T / per_call, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -366,12 +388,14 @@ def run_tier(args):
         "scaling": "weak", "vs_baseline": None,
         "dtype": "int8x" + {2: "int2", 4: "int4", 8: "int8", 40: "mxfp4"}[wl["wbits"]],
         "data": "synthetic (seeded SplitMix64); experts in pinned host RAM, copies inside the timed region",
-        "config": {"workload": wl["name"] + "_tier", "tokens": T, "slots": slots, "n_experts": E,
-                   "stacked_layers": L, "scale_group": wl.get("scale_group", 0)},
+        "config": {"workload": wl["name"] + "_tier" + ("_lookahead" if args.tier_lookahead else ""), "tokens": T,
+                   "slots": slots, "n_experts": E, "stacked_layers": L, "scale_group": wl.get("scale_group", 0),
+                   "residual_sigma": args.tier_residual},
         "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": round(h2d, 2), "unit": "GB/s",
                      "frac": round(achieved / h2d, 4), "traffic": None,
                      "kernel": "host->HBM expert copies (hipMemcpyAsync, overlapped with the resident pairs' FFN)", "bytes_per_step": copy_bytes // args.steps},
         "tier": {"hit_rate": round(hit, 4), "loads_per_call": round(stats["loads"] / calls, 2),
+                 "prefetched_per_call": round(stats["prefetched"] / calls, 2),
                  "union_per_call": round(stats["unions"] / calls, 2)},
     }
     print(json.dumps(line), flush=True)
@@ -504,6 +528,10 @@ def main():
     ap.add_argument("--cmd", type=str, default="", help="the command that produced the profiler output")
     ap.add_argument("--tier-slots", type=int, default=0,
                     help="measure the expert tier instead: experts in pinned host RAM, this many HBM slots per layer")
+    ap.add_argument("--tier-lookahead", action="store_true",
+                    help="with --tier-slots: prefetch each next layer's predicted union (router lookahead)")
+    ap.add_argument("--tier-residual", type=float, default=0.0,
+                    help="with --tier-slots: inputs form a synthetic residual stream, x_l = x_(l-1) + sigma * noise")
     args = ap.parse_args()
 
     if args.summarize_stats:
