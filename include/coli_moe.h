@@ -264,7 +264,10 @@ size_t coli_moe_tier_workspace_bytes(const coli_moe_cfg *cfg, int32_t slots, int
  * host_scales: all E + has_shared experts in pinned host memory. topk_idx_opt / topk_w_opt
  * (device, [T][k]) receive the route (expert ids) when non-NULL. With no misses the whole
  * FFN runs once, as in coli_moe_layer. COLI_E_UNSUPPORTED when the union does not fit
- * (nothing is copied or computed after the route; *tier is unchanged). */
+ * (nothing is copied or computed after the route; *tier is unchanged). After COLI_E_DEVICE
+ * the tier may list experts whose copies did not run: reset it with coli_tier_init. The
+ * tier's arrays and the host experts must stay valid until `stream` and `copy_stream` have
+ * run the call. */
 int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
                           const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
                           const float *x, int32_t T, float *out, int32_t *topk_idx_opt, float *topk_w_opt,
@@ -278,7 +281,8 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
  * call on the same copy_stream waits for these copies before it reads the pool. Waits for
  * `stream` after the route. workspace: coli_moe_tier_workspace_bytes(cfg, tier->slots, T).
  * *n_loaded_opt receives the number of experts copied. COLI_E_UNSUPPORTED when the
- * predicted union does not fit (nothing copied, *tier unchanged). */
+ * predicted union does not fit (nothing copied, *tier unchanged); after COLI_E_DEVICE reset
+ * the tier with coli_tier_init. */
 int coli_moe_tier_prefetch(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
                            const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
                            const float *x, int32_t T, void *workspace, size_t ws_bytes, void *stream,
