@@ -228,7 +228,8 @@ int coli_tier_init(coli_tier *t);
  * the least recently used slot whose expert is neither pinned nor in this union (lowest
  * slot on ties). Outputs (host): slot_idx [T][k] = the route in slot ids (-1 kept);
  * load_expert / load_slot [*n_load] = the misses and their slots (capacity: slots).
- * COLI_E_INVALID for ids outside [-1, E); COLI_E_UNSUPPORTED when the union does not fit
+ * COLI_E_INVALID for ids outside [-1, E) or an inconsistent state (slot_of and expert_in
+ * not inverse to each other); COLI_E_UNSUPPORTED when the union does not fit
  * (more distinct experts than slots that can be freed). On error the state is unchanged. */
 int coli_tier_plan(coli_tier *t, const int32_t *topk_idx, int32_t T, int32_t k, int32_t *slot_idx,
                    int32_t *load_expert, int32_t *load_slot, int32_t *n_load);

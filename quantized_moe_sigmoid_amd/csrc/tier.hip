@@ -37,6 +37,15 @@ int coli_tier_plan(coli_tier *t, const int32_t *topk_idx, int32_t T, int32_t k, 
     if (e < -1 || e >= E) return COLI_E_INVALID;
     if (e >= 0) in_union[e] = 1;
   }
+  // the state must be consistent (caller-owned memory): every index stays in range below
+  for (int32_t s = 0; s < S; s++) {
+    const int32_t e = t->expert_in[s];
+    if (e < -1 || e >= E || (e >= 0 && t->slot_of[e] != s)) return COLI_E_INVALID;
+  }
+  for (int32_t e = 0; e < E; e++) {
+    const int32_t s = t->slot_of[e];
+    if (s < -1 || s >= S || (s >= 0 && t->expert_in[s] != e)) return COLI_E_INVALID;
+  }
   std::vector<int32_t> misses;
   for (int32_t e = 0; e < E; e++)
     if (in_union[e] && t->slot_of[e] < 0) misses.push_back(e);

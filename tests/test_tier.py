@@ -157,3 +157,17 @@ def test_tiered_entry_points_reject_bad_arguments_on_the_host(q):
     t2 = q.Tier(12, 8)
     assert fn(*args(C.byref(t2.c), 4, 1 << 30)) == qq.COLI_E_INVALID        # tier of another layer shape
     assert int(t.c.clock) == 0
+
+
+def test_inconsistent_state_is_rejected(q):
+    import quantized_moe_sigmoid_amd as qq
+    t = q.Tier(8, 3)
+    t.plan(np.array([[1, 2]], np.int32))
+    t.expert_in[0] = 7          # slot 0 claims expert 7, whose slot_of is -1
+    with pytest.raises(qq.ColiError) as ei:
+        t.plan(np.array([[1]], np.int32))
+    assert ei.value.status == qq.COLI_E_INVALID
+    t.expert_in[0] = 1
+    t.slot_of[5] = 9            # out of range
+    with pytest.raises(qq.ColiError):
+        t.plan(np.array([[1]], np.int32))
