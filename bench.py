@@ -154,9 +154,9 @@ def gateup_bytes(wl, U: int, T: int, pairs: int | None = None) -> int:
     S = 1 if wl["has_shared"] else 0
     nexp = U + S
     weights = nexp * 2 * F * (_packed_row_bytes(wl, H) + _row_scale_bytes(wl, H))
-    acts = T * (H + 8 * (H // 32))
+    acts = T * (H + 4 * (H // 32))   # Q8_0 codes + one fp32 scale per 32 values
     rows_out = (T * k if pairs is None else pairs) + S * T
-    hout = rows_out * (F + 8 * (F // 32))
+    hout = rows_out * (F + 4 * (F // 32))
     return weights + acts + hout
 
 
