@@ -129,3 +129,14 @@ def test_argument_errors(q):
     # profiled: wrong event count
     arr = (C.c_void_p * 3)(p, p, p)
     assert L.coli_moe_layer_profiled(C.byref(c), C.byref(w), p, 8, p, p, ws_need, None, arr, 3) == -1
+
+
+def test_header_is_plain_c():
+    """include/coli_moe.h compiles as C99 (no C++ or HIP types in the boundary)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
