@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the routed MoE layer on one MI355X.
 
-A step is one whole layer (route, group, quantise, gate/up, down, combine: every
+A step is one whole layer call (route, group, quantise, gate/up, down, combine: every
 row of the hot path) over one batch of T synthetic tokens, on the stacked layer
 l = step mod L, so that consecutive steps stream different weights (the stack is
-larger than the 256 MB Infinity Cache). Inputs are resident in HBM before the
-timed region. Default workload: the OLMoE-scale decode layer (hidden 2048, expert
-FFN 1024, 64 experts, top-8 sigmoid router, int4 per-row weights, Q8_0
-activations), T = 16, 8 stacked layers; T = 1 and 4 are reported in "sweep".
+larger than the 256 MB Infinity Cache). Inputs are resident in HBM before the timed
+region. Default workload: the GLM-5.2-scale decode layer (hidden 6144, expert FFN
+2048, 256 routed experts + 1 shared, top-8 of 8 groups / 4 kept, routed scaling 2.5,
+int4 per-row weights, Q8_0 activations), 8 stacked layers (about 39 GB), T = 16 as
+the headline (exactly --steps timed layer calls); T = 1, 4 and 16 are reported in
+"sweep" (at least 64 timed calls each), and the GLM-scale batch-union prefill
+(T = 2048, Zipf-skewed router bias) under "prefill" with its int8 TOP/s.
 
 Prints ONE JSON line (rank 0). Extra detail goes to stderr.
 """
@@ -26,7 +29,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, AMD public specification
 DOMINANT_STAGE = "ffn_gate_up"
-KERNEL_SOURCES = ["quantized_moe_sigmoid_amd/csrc/ffn_gemv.hip", "quantized_moe_sigmoid_amd/csrc/ffn_mfma.hip"]
+METRIC = "MoE-layer tokens/s + int4 weight GB/s vs HBM peak (decode); int8 TOPS (prefill)"
+KERNEL_SOURCES = ["quantized_moe_sigmoid_amd/csrc/coli_internal.h", "quantized_moe_sigmoid_amd/csrc/ffn_gemv_impl.h",
+                  "quantized_moe_sigmoid_amd/csrc/ffn_gemv_w4.hip", "quantized_moe_sigmoid_amd/csrc/ffn_mfma.hip"]
 LOCAL_GROUP_MAX_P = 512         # batches above this many (token, expert) pairs take the grouped-GEMM path
 
 
@@ -168,7 +173,12 @@ def layer_weight_bytes(wl, U: int) -> int:
                    H * (_packed_row_bytes(wl, F) + _row_scale_bytes(wl, F)))
 
 
-def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
+def run_T(stack, T: int, n_calls: int, warmup: int, use_graph: bool, n_prof: int | None = None):
+    """Time exactly n_calls layer calls at T tokens (call i on stacked layer i mod L),
+    after `warmup` untimed calls. With use_graph the n_calls calls are captured as one
+    HIP graph and replayed once inside the timed region (the launches cost no host
+    time); the region is bracketed by device synchronisations. A second pass of n_prof
+    calls records HIP events between the stages of each call (per-stage durations)."""
     import torch
     import quantized_moe_sigmoid_amd as q
     xs = stack.inputs(T)
@@ -181,41 +191,38 @@ def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
         l = i % L
         q.layer(stack.cfg, stack.layers[l][1], xs[l], outs[l], ws, stream=stream)
 
-    graph = None
     with torch.cuda.stream(stream):
         for i in range(max(warmup, 1)):
             step(i)
     torch.cuda.synchronize()
+    graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            for i in range(L):
+            for i in range(n_calls):
                 step(i)
         torch.cuda.synchronize()
-        graph.replay()
+        graph.replay()  # untimed: the first replay uploads the graph
         torch.cuda.synchronize()
-    reps = max(1, steps // L) if use_graph else steps
-    nsteps = reps * L if use_graph else steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         if use_graph:
-            for _ in range(reps):
-                graph.replay()
+            graph.replay()
         else:
-            for i in range(steps):
+            for i in range(n_calls):
                 step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / nsteps
+    ms = (t1 - t0) * 1e3 / n_calls
+    del graph
 
-    # Per-stage durations: a second timed pass over the same steps, with HIP events
-    # (no system-scope fence, so recording them costs no cache flush) recorded on the
-    # launch stream between the stages of each layer call.
+    # Per-stage durations: HIP events (no system-scope fence, so recording them costs no
+    # cache flush) recorded on the launch stream between the stages of each layer call.
     ns = q.num_stages()
     names = [q.stage_name(i) for i in range(ns)]
     acc = [0.0] * ns
-    nprof = max(L, (min(steps, 8 * L) // L) * L)
+    nprof = n_prof if n_prof is not None else 4 * L
     ev = q.TimingEvents(ns + 1)
     with torch.cuda.stream(stream):
         for i in range(nprof):
@@ -227,7 +234,7 @@ def run_T(stack, T: int, steps: int, warmup: int, use_graph: bool):
     ev.close()
     stage_ms = {names[s]: acc[s] / nprof for s in range(ns)}
     us, pairs = stack.union_sizes(xs)
-    return dict(T=T, ms=ms, steps=nsteps, stage_ms=stage_ms, U=us, pairs=pairs)
+    return dict(T=T, ms=ms, calls=n_calls, stage_ms=stage_ms, stage_calls=nprof, U=us, pairs=pairs)
 
 
 def copy_bandwidth(mbytes: int, reps: int):
@@ -250,6 +257,28 @@ def copy_bandwidth(mbytes: int, reps: int):
     dt = (time.perf_counter() - t0) / reps
     del src, dst
     return 2 * n / dt / 1e9
+
+
+def read_bandwidth(mbytes: int, reps: int):
+    """Streaming read of mbytes MiB (synth.device.read: 16-byte loads, four in flight per
+    thread, nothing written but one word per wavefront): the measured read-bandwidth
+    ceiling of the device beside the 8 TB/s specification. Returns GB/s."""
+    import torch
+    import synth.device
+    n = mbytes << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(3)
+    sink = synth.device.read_sink(src.device)
+    torch.cuda.synchronize()
+    synth.device.read(src, sink)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        synth.device.read(src, sink)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, sink
+    return n / dt / 1e9
 
 
 def h2d_bandwidth(mbytes: int = 256, reps: int = 5) -> float:
@@ -408,29 +437,78 @@ def gateup_ops(wl, T: int, pairs: float | None = None) -> int:
     return 2 * rows * 2 * wl["ffn"] * wl["hidden"]
 
 
-def cpu_baseline(stack, T: int, budget_s: float):
-    """The oracle (plain C, OpenMP) timed on host cores on layer 0 of the same workload
-    (at most 64 tokens of it: a bounded sample of a large batch)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sample(wl, seed: int, T: int):
+    """Inputs of the oracle for T tokens of layer 0, with host copies of only the experts
+    these tokens route to (the route is computed once here to find them)."""
     import numpy as np
     import oracle
     import synth
-    wl = stack.wl
-    seed, _ = stack.layers[0]
-    T = min(T, 64)
     inp = synth.layer_inputs(seed, 0, tokens=T, hidden=wl["hidden"], ffn=wl["ffn"], n_experts=wl["n_experts"],
                              has_shared=wl["has_shared"], wbits=wl["wbits"], zipf=wl.get("zipf", False),
-                             scale_group=wl.get("scale_group", 0))
+                             with_blobs=False, scale_group=wl.get("scale_group", 0))
     cfg = oracle.make_cfg(**wl)
+    ridx, _ = oracle.route(cfg, inp["router_w"], inp["router_bias"], inp["x"])
+    E, S = wl["n_experts"], 1 if wl["has_shared"] else 0
+    need = sorted(set(int(e) for e in ridx.ravel() if e >= 0))
+    remap = np.full(E + 1, -1, np.int32)
+    remap[need] = np.arange(len(need), dtype=np.int32)
+    rows = need + ([E] if S else [])
+    blobs = np.stack([synth.expert_blob(seed, 0, e, wl["hidden"], wl["ffn"], wl["wbits"]) for e in rows])
+    scales = np.ascontiguousarray(inp["scales"][rows])
+    sub = oracle.make_cfg(**dict(wl, n_experts=len(need), n_group=1, topk_group=1))
+    return dict(cfg=cfg, sub=sub, inp=inp, blobs=blobs, scales=scales, remap=remap)
+
+
+def _time_oracle(smp, budget_s: float):
+    """Oracle layer calls (route, then the FFN of the routed experts and the combine) until
+    budget_s has passed; returns (calls, seconds)."""
+    import oracle
+    inp = smp["inp"]
     calls = 0
     t0 = time.perf_counter()
     while True:
-        oracle.layer(cfg, inp["blobs"], inp["scales"], inp["router_w"], inp["router_bias"], inp["x"])
+        idx, w = oracle.route(smp["cfg"], inp["router_w"], inp["router_bias"], inp["x"])
+        oracle.ffn(smp["sub"], smp["blobs"], smp["scales"], inp["x"], smp["remap"][idx], w)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return dict(value=T * calls / el, unit="tokens/s", cores=oracle.threads(), kind="oracle",
-                sample=f"{calls} oracle calls of layer 0 at T={T} ({el:.1f} s wall)")
+            return calls, el
+
+
+def cpu_baseline(stack, T: int, budget_s: float, budget_1t_s: float):
+    """The oracle (plain C, OpenMP over tokens, untuned) timed on the host cores on layer 0
+    of the same workload and inputs: at the headline T with every OpenMP thread, and at
+    T = 1 on a single thread (each a bounded sample of about the given seconds)."""
+    import oracle
+    wl = stack.wl
+    seed, _ = stack.layers[0]
+    Tm = min(T, 64)
+    threads = oracle.threads()
+    calls, el = _time_oracle(_oracle_sample(wl, seed, Tm), budget_s)
+    res = dict(value=Tm * calls / el, unit="tokens/s", cores=threads, kind="oracle",
+               sample=f"{calls} oracle calls of layer 0 at T={Tm} on {threads} threads ({el:.1f} s wall)",
+               cpu_model=_cpu_model(), nproc=os.cpu_count(), omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+    if budget_1t_s > 0:
+        smp1 = _oracle_sample(wl, seed, 1)
+        oracle.set_threads(1)
+        try:
+            c1, e1 = _time_oracle(smp1, budget_1t_s)
+        finally:
+            oracle.set_threads(threads)
+        res["single_thread"] = dict(value=c1 / e1, unit="tokens/s", cores=1,
+                                    sample=f"{c1} oracle calls of layer 0 at T=1 on 1 thread ({e1:.1f} s wall)")
+    return res
 
 
 def _csv_rows(path_or_dir: str, suffix: str):
@@ -502,12 +580,79 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, calib_mb: int, cmd: 
     print(json.dumps(d, indent=1))
 
 
+def down_ops(wl, T: int, pairs: float | None = None) -> int:
+    """int8 operations (x2) of one down launch: every pair row against H rows of F inputs."""
+    rows = (T * wl["top_k"] if pairs is None else pairs) + (T if wl["has_shared"] else 0)
+    return 2 * rows * wl["hidden"] * wl["ffn"]
+
+
+def summarize_T(wl, r):
+    """Derived figures of one run_T result: tokens/s, gate/up bytes and GB/s, layer weight
+    bytes and GB/s (the int4 weights + scales the call streams, against the HBM peak)."""
+    U = sum(r["U"]) / len(r["U"])
+    r["U_mean"] = U
+    r["tok_s"] = r["T"] / (r["ms"] * 1e-3)
+    gu_ms = r["stage_ms"][DOMINANT_STAGE]
+    gb = sum(gateup_bytes(wl, u, r["T"], pr) for u, pr in zip(r["U"], r["pairs"])) / len(r["U"])
+    r["gateup_bytes"] = gb
+    r["gateup_gbs"] = gb / (gu_ms * 1e-3) / 1e9
+    lw = sum(layer_weight_bytes(wl, u) for u in r["U"]) / len(r["U"])
+    r["layer_weight_bytes"] = lw
+    r["layer_weight_gbs"] = lw / (r["ms"] * 1e-3) / 1e9
+    return r
+
+
+def sweep_entry(r):
+    return {"T": r["T"], "calls": r["calls"], "tokens_per_s": round(r["tok_s"], 1),
+            "us_per_step": round(r["ms"] * 1e3, 2), "U_mean": r["U_mean"],
+            "pairs_mean": sum(r["pairs"]) / len(r["pairs"]), "gate_up_GBps": round(r["gateup_gbs"], 1),
+            "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
+            "layer_weight_frac": round(r["layer_weight_gbs"] / HBM_PEAK_GBS, 4),
+            "stage_calls": r["stage_calls"], "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}}
+
+
+def prefill_leg(args, n_calls: int):
+    """The batch-union prefill workload (T = 2048 on one layer whose 4.9 GB of weights
+    exceed every cache), timed in the same run: tokens/s per layer and int8 TOP/s of the
+    gate/up and down grouped GEMMs against the 5.0 POP/s dense int8 peak."""
+    import synth
+    stack = Stack(args.prefill_config, 1, args.wbits, args.scale_group, args.topp)
+    wl = stack.wl
+    T = wl["tokens"][-1]
+    r = summarize_T(wl, run_T(stack, T, n_calls, args.warmup, not args.no_graph, n_prof=8))
+    pairs = sum(r["pairs"]) / len(r["pairs"])
+    gu_ms, dn_ms = r["stage_ms"][DOMINANT_STAGE], r["stage_ms"]["ffn_down"]
+    gops, dops = gateup_ops(wl, T, pairs), down_ops(wl, T, pairs)
+    gtops, dtops = gops / (gu_ms * 1e-3) / 1e12, dops / (dn_ms * 1e-3) / 1e12
+    layer_tops = (gops + dops) / (r["ms"] * 1e-3) / 1e12
+    log(f"prefill T={T}: {r['ms']*1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, U={r['U_mean']:.1f}, gate/up "
+        f"{gu_ms*1e3:.1f} us = {gtops:.0f} TOP/s, down {dn_ms*1e3:.1f} us = {dtops:.0f} TOP/s; stages(us) " +
+        ", ".join(f"{k}={v*1e3:.1f}" for k, v in r["stage_ms"].items()))
+    out = {"workload": wl["name"], "tokens": T, "calls": n_calls, "tokens_per_s": round(r["tok_s"], 1),
+           "us_per_step": round(r["ms"] * 1e3, 2), "U_mean": r["U_mean"], "pairs_mean": pairs,
+           "gate_up": {"kernel": "mfma_kernel (grouped GEMM, v_mfma_i32_32x32x32_i8)", "ops_per_launch": int(gops),
+                       "avg_launch_us": round(gu_ms * 1e3, 2), "achieved_TOPs": round(gtops, 1),
+                       "peak_TOPs": INT8_PEAK_TOPS, "frac": round(gtops / INT8_PEAK_TOPS, 4),
+                       "traffic": read_traffic(wl["name"], T), "weight_GBps": round(r["gateup_gbs"], 1)},
+           "down": {"ops_per_launch": int(dops), "avg_launch_us": round(dn_ms * 1e3, 2),
+                    "achieved_TOPs": round(dtops, 1), "frac": round(dtops / INT8_PEAK_TOPS, 4)},
+           "layer_TOPs": round(layer_tops, 1), "layer_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
+           "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
+           "stage_calls": r["stage_calls"], "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}}
+    del stack
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--steps", type=int, default=200, help="timed layer calls at the headline T")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
+                    help="workload: 1 OLMoE-scale decode, 2 GLM-scale decode (default), 3 GLM-scale prefill, "
+                         "4 verify / low-bit")
+    ap.add_argument("--prefill-config", type=int, default=3, choices=[0, 3],
+                    help="prefill leg timed in the same run (0: none)")
     ap.add_argument("--wbits", type=int, default=None, choices=[2, 4, 8, 40],
                     help="weight format: int2/int4/int8, or 40 = MXFP4 (E2M1 codes, E8M0 scale per 32 inputs)")
     ap.add_argument("--topp", type=float, default=0.0,
@@ -516,11 +661,13 @@ def main():
                     help="64: group-scaled weights, one fp32 scale per 64 inputs of a row")
     ap.add_argument("--tokens", type=str, default=None, help="comma list of T; the last is the headline")
     ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--sweep-calls", type=int, default=64, help="timed calls per T of the sweep (at least)")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget-1t", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-mb", type=int, default=1024,
-                    help="MiB moved by the copy kernel that calibrates byte counters (0: skip)")
+                    help="MiB moved by the copy and read kernels (byte-counter calibration, bandwidth ceilings; 0: skip)")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
                     help="write a short text summary of a rocprofv3 --stats kernel table and exit")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
@@ -545,38 +692,36 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's sharding across GPUs "
               "is a design note, not built", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        raise SystemExit("--steps must be at least 1")
 
     if args.tier_slots:
         run_tier(args)
         return
 
     import synth
-    copy_gbs = None
+    copy_gbs = read_gbs = None
     if args.calib_mb > 0:
         copy_gbs = copy_bandwidth(args.calib_mb, 5)
-        log(f"copy kernel ({args.calib_mb} MiB): {copy_gbs:.0f} GB/s read+write")
+        read_gbs = read_bandwidth(args.calib_mb, 5)
+        log(f"copy kernel ({args.calib_mb} MiB): {copy_gbs:.0f} GB/s read+write; read kernel: {read_gbs:.0f} GB/s")
     wl0 = synth.WORKLOADS[args.config]
     Ts = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl0["tokens"])
-    stack = Stack(args.config, args.layers, args.wbits, args.scale_group, args.topp)
+    layers = args.layers if len(wl0["tokens"]) > 1 or wl0["tokens"][0] < 1024 else 1
+    stack = Stack(args.config, layers, args.wbits, args.scale_group, args.topp)
     wl = stack.wl
     results = []
     for T in Ts:
-        r = run_T(stack, T, args.steps, args.warmup, not args.no_graph)
-        U = sum(r["U"]) / len(r["U"])
-        r["U_mean"] = U
-        r["tok_s"] = T / (r["ms"] * 1e-3)
-        gu_ms = r["stage_ms"][DOMINANT_STAGE]
-        # algorithmic bytes of the dominant kernel per launch, averaged over the stacked layers
-        gb = sum(gateup_bytes(wl, u, T, pr) for u, pr in zip(r["U"], r["pairs"])) / len(r["U"])
-        r["gateup_bytes"] = gb
-        r["gateup_gbs"] = gb / (gu_ms * 1e-3) / 1e9
-        r["layer_weight_gbs"] = (sum(layer_weight_bytes(wl, u) for u in r["U"]) / len(r["U"])) / (r["ms"] * 1e-3) / 1e9
+        r = summarize_T(wl, run_T(stack, T, max(args.steps, args.sweep_calls), args.warmup, not args.no_graph))
         results.append(r)
-        log(f"T={T}: {r['ms']*1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, U={U:.1f}, gate/up {gu_ms*1e3:.1f} us "
-            f"= {r['gateup_gbs']:.0f} GB/s, layer weights {r['layer_weight_gbs']:.0f} GB/s; stages(us) " +
+        log(f"T={T}: {r['ms']*1e3:.1f} us/step over {r['calls']} calls, {r['tok_s']:.0f} tok/s, U={r['U_mean']:.1f}, "
+            f"gate/up {r['stage_ms'][DOMINANT_STAGE]*1e3:.1f} us = {r['gateup_gbs']:.0f} GB/s, layer weights "
+            f"{r['layer_weight_gbs']:.0f} GB/s ({r['layer_weight_gbs'] / HBM_PEAK_GBS:.2f} of peak); stages(us) " +
             ", ".join(f"{k}={v*1e3:.1f}" for k, v in r["stage_ms"].items()))
-    head = results[-1]
-    T = head["T"]
+    # the headline: exactly --steps timed layer calls at the last T
+    T = Ts[-1]
+    head = summarize_T(wl, run_T(stack, T, args.steps, args.warmup, not args.no_graph))
+    log(f"headline T={T}: {head['ms']*1e3:.1f} us/step over exactly {args.steps} calls, {head['tok_s']:.0f} tok/s")
     gemm = T * wl["top_k"] > LOCAL_GROUP_MAX_P
     gu_ms = head["stage_ms"][DOMINANT_STAGE]
     traffic = read_traffic(wl["name"], T)
@@ -586,26 +731,31 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic,
                 "kernel": "mfma_kernel (gate/up grouped GEMM, v_mfma_i32_32x32x32_i8)",
-                "ops_per_launch": ops, "avg_launch_us": round(gu_ms * 1e3, 2),
-                "gate_up_GBps": round(head["gateup_gbs"], 1),
-                "measured_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1)}
+                "ops_per_launch": ops, "avg_launch_us": round(gu_ms * 1e3, 2)}
     else:
         ach = head["gateup_gbs"]
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gate/up GEMV (fused SiLU*up + Q8_0 requantisation)",
-                "bytes_per_launch": int(head["gateup_bytes"]), "avg_launch_us": round(gu_ms * 1e3, 2),
-                "measured_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1)}
+                "bytes_per_launch": int(head["gateup_bytes"]), "avg_launch_us": round(gu_ms * 1e3, 2)}
+    roof.update({"launches_timed": head["stage_calls"],
+                 "measured_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
+                 "measured_read_GBps": None if read_gbs is None else round(read_gbs, 1),
+                 "layer_weight_GBps": round(head["layer_weight_gbs"], 1),
+                 "layer_weight_frac": round(head["layer_weight_gbs"] / HBM_PEAK_GBS, 4)})
+    prefill = None
+    if args.prefill_config and not gemm:
+        prefill = prefill_leg(args, max(args.steps // 4, 50))
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(stack, T, args.cpu_budget)
+        cpu = cpu_baseline(stack, T, args.cpu_budget, args.cpu_budget_1t)
         log(f"cpu baseline: {cpu}")
     line = {
-        "metric": "MoE-layer tokens/s (" + ("prefill" if gemm else "decode") + ")",
+        "metric": METRIC,
         "value": round(head["tok_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": head["steps"],
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["ms"], 5),
         "higher_is_better": True,
@@ -615,16 +765,13 @@ def main():
         "data": "synthetic (seeded SplitMix64; random int weights, N(0,1) activations)",
         "config": {"workload": wl["name"], "hidden": wl["hidden"], "ffn": wl["ffn"], "n_experts": wl["n_experts"],
                    "top_k": wl["top_k"], "n_group": wl["n_group"], "topk_group": wl["topk_group"],
-                   "has_shared": wl["has_shared"], "wbits": wl["wbits"],
+                   "rsf": wl["rsf"], "has_shared": wl["has_shared"], "wbits": wl["wbits"],
                    "scale_group": wl.get("scale_group", 0), "topp": wl.get("topp", 0.0), "tokens": T,
                    "stacked_layers": stack.L, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "sweep": [{"T": r["T"], "tokens_per_s": round(r["tok_s"], 1), "us_per_step": round(r["ms"] * 1e3, 2),
-                   "U_mean": r["U_mean"], "pairs_mean": sum(r["pairs"]) / len(r["pairs"]),
-                   "gate_up_GBps": round(r["gateup_gbs"], 1),
-                   "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
-                   "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}} for r in results],
+        "sweep": [sweep_entry(r) for r in results],
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

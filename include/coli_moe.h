@@ -5,8 +5,8 @@
  * The layer, as the Colibri pages state it:
  *   - router: DeepSeek-V3-style sigmoid router, noaux_tc, routed_scaling_factor,
  *     plus a shared expert (colibri-strix README, "What's implemented", router item);
- *   - batch-union: every distinct expert of the batch is read once and applied to
- *     every position routed to it (colibri-strix README, "What's implemented",
+ *   - batch-union: the weights of an expert are fetched a single time per batch,
+ *     however many tokens chose it (colibri-strix README, "What's implemented",
  *     batch-union item; JustVugg/colibri README, "Never wait for the disk twice");
  *   - quantised experts: int8 / packed int4 / packed int2 weights with per-row
  *     scales, dequantised on use (colibri-strix README, "What's implemented",
@@ -144,8 +144,8 @@ int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q
 /* Sigmoid noaux_tc router for T tokens: topk_idx int32 [T][k] (expert ids, slot
  * order), topk_w fp32 [T][k]. Uses the workspace for fp64 logits.
  * Follows colibri-strix README, "What's implemented", router item.
- * With cfg->topp > 0 (adaptive expert top-p, JustVugg/colibri README, "Useful knobs",
- * --topp; opt-in, it changes the router's result): only the shortest prefix of the k
+ * With cfg->topp > 0 (adaptive expert top-p, the --topp knob of the colibri-strix README,
+ * "Experimental resident CUDA backend", useful-knobs paragraph; opt-in, it changes the router's result): only the shortest prefix of the k
  * slots whose scores s sum (fp64, slot order) to at least topp times the k slots' sum
  * is kept, at least one slot; the kept weights are s_j / (that prefix sum) * rsf, and
  * every dropped slot holds index -1 and weight 0. */

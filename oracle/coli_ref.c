@@ -304,8 +304,8 @@ int coli_ref_moe_route(const coli_ref_cfg *cfg, const float *router_w, const flo
 }
 
 /* ------------------------------------------------------------------- group --
- * colibri-strix README, "What's implemented", batch-union item: each distinct
- * expert of the batch is read once and applied to every position routed to it.
+ * colibri-strix README, "What's implemented", batch-union item: the weights of an
+ * expert are fetched a single time per batch, however many tokens chose it.
  * The grouping lists, per expert, its pairs p = t*k + j in ascending p (a stable
  * counting sort by expert), the exclusive offsets into that list, and the
  * experts that received at least one pair, ascending. */

@@ -80,7 +80,8 @@ int coli_ref_pack(int32_t wbits, const int8_t *q, int64_t n, uint8_t *out);
 int coli_ref_unpack(int32_t wbits, const uint8_t *in, int64_t n, int8_t *q);
 
 /* Router for T tokens: topk_idx int32 [T, k], topk_w fp32 [T, k]. With topp > 0 (adaptive
- * expert top-p, JustVugg/colibri README, "Useful knobs", --topp) only the shortest prefix of the
+ * expert top-p, the --topp knob of the colibri-strix README, "Experimental resident CUDA backend",
+ * useful-knobs paragraph) only the shortest prefix of the
  * k slots whose summed scores reach topp of the k slots' sum is kept (at least one slot); the
  * kept weights are renormalised over the kept slots and the dropped slots hold index -1 and
  * weight 0. The grouping and the FFN skip index -1. */

@@ -108,9 +108,33 @@ struct FfnArgs {
   int8_t *hq;         // [P+T][F]
   float *hd;          // [P+T][F/32]
   float *ypair;       // [P+T][H]
+  float *tap;         // test builds (COLI_TAPS) only: [P+T][2F] pre-SiLU g | u per output row
 };
+
+// Test builds (compiled with COLI_TAPS) record the gate and up values of every output
+// row before SiLU (row scale applied, fp32, exactly as the epilogue uses them). Product
+// builds compile this to nothing.
+#ifdef COLI_TAPS
+#define COLI_TAP_GU(a, row, f, gv, uv)                                    \
+  do {                                                                   \
+    if ((a).tap) {                                                       \
+      (a).tap[(int64_t)(row) * 2 * (a).F + (f)] = (gv);                  \
+      (a).tap[(int64_t)(row) * 2 * (a).F + (a).F + (f)] = (uv);          \
+    }                                                                    \
+  } while (0)
+#else
+#define COLI_TAP_GU(a, row, f, gv, uv) \
+  do {                                 \
+  } while (0)
+#endif
 hipError_t launch_gateup(int wfmt, const FfnArgs &a, hipStream_t s);
 hipError_t launch_down(int wfmt, const FfnArgs &a, hipStream_t s);
+// per-format GEMV launchers (ffn_gemv_w4/w8/w2/mx.hip); mode 0 = gate/up, 1 = down;
+// gs: group-scale path (MXFP4 always takes it)
+hipError_t launch_gemv_w4(int mode, bool gs, const FfnArgs &a, hipStream_t s);
+hipError_t launch_gemv_w8(int mode, bool gs, const FfnArgs &a, hipStream_t s);
+hipError_t launch_gemv_w2(int mode, bool gs, const FfnArgs &a, hipStream_t s);
+hipError_t launch_gemv_mx(int mode, const FfnArgs &a, hipStream_t s);
 // grouped-GEMM (MFMA) path for batches whose experts see many tokens
 int32_t mfma_gmax(int32_t T, int32_t k, int32_t E, int32_t has_shared);  // token-tile capacity
 hipError_t launch_plan(const FfnArgs &a, int4 *tiles, int32_t *ntiles, int32_t gmax, hipStream_t s);

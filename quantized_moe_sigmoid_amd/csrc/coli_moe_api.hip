@@ -4,6 +4,9 @@
 #include <limits.h>
 
 #include "coli_internal.h"
+#ifdef COLI_TAPS
+#include "../../include/coli_moe_taps.h"
+#endif
 
 namespace coli {
 
@@ -95,7 +98,7 @@ static Tp *at(void *ws, size_t off) {
 static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const float *x, int32_t T,
                        const float *topk_w, const int32_t *off, const int32_t *perm, const int32_t *active,
                        const int32_t *nact, const int32_t *local_idx, float *out, void *ws, const WsLayout &L,
-                       hipStream_t s, hipEvent_t *ev, bool quantize_x) {
+                       hipStream_t s, hipEvent_t *ev, bool quantize_x, float *tap = nullptr) {
   int st;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
   if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), at<float>(ws, L.xd), s))))
@@ -122,6 +125,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.hq = at<int8_t>(ws, L.hq);
   a.hd = at<float>(ws, L.hd);
   a.ypair = at<float>(ws, L.ypair);
+  a.tap = tap;
   // Batches past the decode size run the expert FFNs as grouped GEMMs on the
   // matrix cores; a tile plan of the union comes first.
   const bool gemm = local_idx == nullptr && (int64_t)T * c.top_k > LOCAL_GROUP_MAX_P;
@@ -145,7 +149,8 @@ static const char *const kStages[] = {"route_logits", "route_select", "group", "
 static constexpr int kNumStages = 7;
 
 static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
-                      int32_t *idx_opt, float *w_opt, void *ws, size_t ws_bytes, void *stream, hipEvent_t *ev) {
+                      int32_t *idx_opt, float *w_opt, void *ws, size_t ws_bytes, void *stream, hipEvent_t *ev,
+                      float *tap = nullptr) {
   int st;
   if ((st = check_cfg(cfg))) return st;
   if ((st = check_T(cfg, T))) return st;
@@ -182,7 +187,7 @@ static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const 
   if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
   if (!local && (st = dev(launch_group(*cfg, idx, T, cnt, off, perm, act, nact, s)))) return st;
   return ffn_enqueue(*cfg, *w, x, T, tw, off, perm, act, nact, local ? idx : nullptr, out, ws, L, s,
-                     ev ? ev + 3 : nullptr, false);
+                     ev ? ev + 3 : nullptr, false, tap);
 }
 
 }  // namespace coli
@@ -205,14 +210,15 @@ size_t coli_moe_scales_per_expert(const coli_moe_cfg *cfg) {
 
 size_t coli_moe_workspace_bytes(const coli_moe_cfg *cfg, int32_t T_max) {
   if (check_cfg(cfg) != COLI_OK || check_T(cfg, T_max) != COLI_OK) return 0;
-  // the K split of the router depends on T: take the largest over T <= T_max
-  size_t best = 0;
-  const int32_t cand[2] = {T_max < 16 ? T_max : 16, T_max};
-  for (int i = 0; i < 2; i++) {
-    const WsLayout L = ws_layout(*cfg, T_max, route_ksplit(*cfg, cand[i]));
-    if (L.total > best) best = L.total;
+  // A call with T tokens needs ws_layout(T, K split of T). Every region grows with T and
+  // with the K split, but the K split shrinks as T grows, so size for T_max tokens with
+  // the largest K split of any T <= T_max: that covers every call up to T_max.
+  int32_t ks = 1;
+  for (int32_t T = 1; T <= T_max; T++) {
+    const int32_t k = route_ksplit(*cfg, T);
+    if (k > ks) ks = k;
   }
-  return best;
+  return ws_layout(*cfg, T_max, ks).total;
 }
 
 int coli_moe_quantize_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, void *stream) {
@@ -264,10 +270,10 @@ int coli_moe_group(const coli_moe_cfg *cfg, const int32_t *topk_idx, int32_t T, 
                           static_cast<hipStream_t>(stream)));
 }
 
-int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
-                 const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm,
-                 const int32_t *active, const int32_t *n_active, float *out, void *workspace, size_t ws_bytes,
-                 void *stream) {
+static int ffn_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                    const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm,
+                    const int32_t *active, const int32_t *n_active, float *out, void *workspace, size_t ws_bytes,
+                    void *stream, float *tap) {
   int st;
   if ((st = check_cfg(cfg))) return st;
   if ((st = check_T(cfg, T))) return st;
@@ -282,7 +288,15 @@ int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float
   if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
   if (!aligned(workspace, 256)) return COLI_E_ALIGN;
   return ffn_enqueue(*cfg, *w, x, T, topk_w, expert_off, pair_perm, active, n_active, nullptr, out, workspace, L,
-                     static_cast<hipStream_t>(stream), nullptr, true);
+                     static_cast<hipStream_t>(stream), nullptr, true, tap);
+}
+
+int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                 const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm,
+                 const int32_t *active, const int32_t *n_active, float *out, void *workspace, size_t ws_bytes,
+                 void *stream) {
+  return ffn_impl(cfg, w, x, T, topk_idx, topk_w, expert_off, pair_perm, active, n_active, out, workspace, ws_bytes,
+                  stream, nullptr);
 }
 
 int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
@@ -299,6 +313,24 @@ int coli_moe_layer_profiled(const coli_moe_cfg *cfg, const coli_moe_weights *w, 
   return layer_impl(cfg, w, x, T, out, nullptr, nullptr, workspace, ws_bytes, stream,
                     reinterpret_cast<hipEvent_t *>(events));
 }
+
+#ifdef COLI_TAPS
+int coli_moe_layer_taps(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                        int32_t *topk_idx_opt, float *topk_w_opt, float *tap_gu, void *workspace, size_t ws_bytes,
+                        void *stream) {
+  if (!tap_gu || !aligned(tap_gu, 4)) return COLI_E_INVALID;
+  return layer_impl(cfg, w, x, T, out, topk_idx_opt, topk_w_opt, workspace, ws_bytes, stream, nullptr, tap_gu);
+}
+
+int coli_moe_ffn_taps(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
+                      const int32_t *topk_idx, const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm,
+                      const int32_t *active, const int32_t *n_active, float *out, float *tap_gu, void *workspace,
+                      size_t ws_bytes, void *stream) {
+  if (!tap_gu || !aligned(tap_gu, 4)) return COLI_E_INVALID;
+  return ffn_impl(cfg, w, x, T, topk_idx, topk_w, expert_off, pair_perm, active, n_active, out, workspace, ws_bytes,
+                  stream, tap_gu);
+}
+#endif
 
 int coli_moe_num_stages(void) { return kNumStages; }
 

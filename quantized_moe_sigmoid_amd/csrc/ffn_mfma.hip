@@ -404,6 +404,7 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       const int f = rbase + 8 * (r >> 2) + 4 * grp + (r & 3);
       const float gv = (GS ? 1.0f : sc[f]) * acc[0][r];
       const float uv = (GS ? 1.0f : sc[a.F + f]) * acc[1][r];
+      if (valid) COLI_TAP_GU(a, out_row, f, gv, uv);
       h[r] = (gv / (1.0f + expf(-gv))) * uv;
       amax = fmaxf(amax, fabsf(h[r]));
     }

@@ -2,8 +2,8 @@
 // by the standalone grouping kernel (1024 threads) and the fused tail of the
 // routing kernel (256 threads).
 //
-// colibri-strix README, "What's implemented", batch-union item: each distinct
-// expert of the batch is read once and applied to every position routed to it.
+// colibri-strix README, "What's implemented", batch-union item: the weights of an
+// expert are fetched a single time per batch, however many tokens chose it.
 // The route (pair p = t*k + j -> expert) becomes per-expert segments: counts,
 // exclusive offsets, the pair ids of each expert in ascending p (a stable counting
 // sort), and the list of experts with work, ascending.

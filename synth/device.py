@@ -36,6 +36,9 @@ def lib():
         L.coli_synth_fill_blobs.restype = C.c_int
         L.coli_synth_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
         L.coli_synth_copy.restype = C.c_int
+        L.coli_synth_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+        L.coli_synth_read.restype = C.c_int
+        L.coli_synth_read_sink_words.restype = C.c_int
         _lib = L
     return _lib
 
@@ -70,3 +73,24 @@ def copy(src, dst, stream=None):
     rc = lib().coli_synth_copy(C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()), nbytes, C.c_void_p(s.cuda_stream))
     if rc != 0:
         raise RuntimeError(f"coli_synth_copy failed: {rc}")
+
+
+def read_sink(device):
+    """A device buffer for read()'s per-wavefront words."""
+    import torch
+    return torch.empty(lib().coli_synth_read_sink_words(), dtype=torch.int32, device=device)
+
+
+def read(src, sink, stream=None):
+    """Streaming device read of ``src`` (byte size a multiple of 16): the measured read
+    bandwidth ceiling. ``sink`` from read_sink() receives one word per wavefront."""
+    import torch
+
+    assert src.is_cuda and src.is_contiguous() and sink.is_cuda
+    assert sink.numel() * sink.element_size() >= 4 * lib().coli_synth_read_sink_words()
+    nbytes = src.numel() * src.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(src.device)
+    rc = lib().coli_synth_read(C.c_void_p(src.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
+                               C.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"coli_synth_read failed: {rc}")

@@ -47,7 +47,40 @@ __global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ d
     dst[g] = src[g];
 }
 
+// Plain streaming read of n16 16-byte words (four loads in flight per thread): the
+// measured read-bandwidth ceiling beside the HBM specification. Each wavefront folds
+// what it read into one word of `sink` ([gridDim.x * 4]), so the loads are not elided.
+__global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src, int64_t n16,
+                                                   uint32_t *__restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; g + 3 * stride < n16; g += 4 * stride) {
+    const uint4 a = src[g], b = src[g + stride], c = src[g + 2 * stride], d = src[g + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; g < n16; g += stride) {
+    const uint4 a = src[g];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
 }  // namespace
+
+constexpr int kReadGrid = 4096;
+
+extern "C" int coli_synth_read_sink_words(void) { return kReadGrid * 4; }
+
+extern "C" int coli_synth_read(const void *src, int64_t bytes, void *sink, void *stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16) return -1;
+  if (((uintptr_t)src % 16) != 0 || ((uintptr_t)sink % 4) != 0) return -4;
+  hipLaunchKernelGGL(read_kernel, dim3(kReadGrid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int coli_synth_copy(const void *src, void *dst, int64_t bytes, void *stream) {
   if (!src || !dst || bytes <= 0 || bytes % 16) return -1;

@@ -140,3 +140,36 @@ def test_header_is_plain_c():
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_workspace_query_covers_every_smaller_batch(q):
+    """The workspace for T_max tokens also covers every T <= T_max: the query never shrinks
+    as T_max grows (the router's K split shrinks with T while the batch grows)."""
+    for cfgd in (dict(hidden=256, ffn=128, n_experts=256, top_k=4), dict(hidden=256, ffn=128, n_experts=16, top_k=4),
+                 dict(hidden=6144, ffn=2048, n_experts=256, top_k=8, n_group=8, topk_group=4, has_shared=True),
+                 dict(hidden=384, ffn=256, n_experts=24, top_k=5, n_group=8, topk_group=3, has_shared=True)):
+        c = q.make_cfg(**cfgd)
+        Tmax = min(5000, 65535 // cfgd["top_k"])
+        sizes = [q.workspace_bytes(c, T) for T in range(1, Tmax + 1, 7)]
+        assert all(s > 0 for s in sizes)
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), cfgd
+
+
+def test_taps_library_exports_only_in_test_build():
+    """libcolimoe_taps.so (COLI_TAPS) exports the product symbols plus the taps entry points of
+    include/coli_moe_taps.h; the product library exports no taps symbol."""
+    import quantized_moe_sigmoid_amd as q
+    from quantized_moe_sigmoid_amd import taps
+    if not os.path.exists(taps.TAPS_LIB_PATH):
+        from quantized_moe_sigmoid_amd import build
+        build.build()
+    src = open(os.path.join(ROOT, "include", "coli_moe_taps.h")).read()
+    names = sorted(set(re.findall(r"\b(coli_moe_\w+_taps)\s*\(", src)))
+    assert names == ["coli_moe_ffn_taps", "coli_moe_layer_taps"]
+    T = taps.lib()
+    for n in names + _declared():
+        assert hasattr(T, n), n
+    prod = C.CDLL(q.LIB_PATH)
+    for n in names:
+        assert not hasattr(prod, n), n
+    assert set(taps.TAP_EXPORTS) == set(names)

@@ -83,12 +83,16 @@ def test_olmoe_decode_full(env):
 
 
 def test_glm_decode_full(env):
-    for T in (1, 16):
-        _run(env, 2, T, [0, T // 2, T - 1])
+    for T in (1, 4, 16):
+        _run(env, 2, T, range(T))
+
+
+# 16 of the 2048 prefill tokens, spread over the batch (the first and the last included)
+PREFILL_SAMPLE = [0, 1, 2, 131, 262, 511, 512, 777, 1023, 1024, 1300, 1536, 1801, 2000, 2046, 2047]
 
 
 def test_glm_prefill_full_sampled(env):
-    _, idx = _run(env, 3, 2048, [0, 1, 777, 2047])
+    _, idx = _run(env, 3, 2048, PREFILL_SAMPLE)
     cnt = np.bincount(idx.ravel(), minlength=256)
     assert cnt.max() > 100 and (cnt == 0).sum() >= 1, (cnt.max(), (cnt == 0).sum())
 
@@ -109,7 +113,7 @@ def test_decode_full_other_scale_formats(env, fmt):
 @pytest.mark.parametrize("fmt", ["gs64", "mxfp4"])
 def test_glm_prefill_full_sampled_other_scale_formats(env, fmt):
     kw = dict(scale_group=64) if fmt == "gs64" else dict(wbits=synth.W_MXFP4)
-    _run(env, 3, 2048, [0, 1, 777, 2047], **kw)
+    _run(env, 3, 2048, PREFILL_SAMPLE, **kw)
 
 
 def test_graph_replay_matches_eager(env):

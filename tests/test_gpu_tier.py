@@ -104,8 +104,10 @@ def test_layer_tiered_overlapped_bitidentical(q, wbits, sg, Ts, slots):
     """coli_moe_layer_tiered: the misses copy on a second stream while the resident pairs
     compute; batch after batch the output and the route equal the resident layer's, bit
     for bit (T >= 150: grouped GEMMs, after small batches that leave part of the union
-    resident)."""
+    resident), and every batch matches the oracle: route bit-exact, weights within one
+    ulp, output within the 1e-3 per-token bar."""
     import torch
+    import oracle
     d = gu.dev()
     T = max(Ts)
     E = 32 if T < 100 else 36
@@ -137,9 +139,15 @@ def test_layer_tiered_overlapped_bitidentical(q, wbits, sg, Ts, slots):
         q.layer_tiered(cfg, resident, tier, hb, hs, pool_b, pool_s, x, out, ws, cs, ev, idx, tw)
         ref, ridx, rw = gu.run_layer(cfgd, resident, x_np)
         torch.cuda.synchronize()
+        got = out.cpu().numpy()
         assert np.array_equal(idx.cpu().numpy(), ridx)
         assert np.array_equal(tw.cpu().numpy().view(np.uint32), rw.view(np.uint32))
-        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), bi
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), bi
+        oref, oidx, ow = oracle.layer(oracle.make_cfg(**cfgd), inp["blobs"], inp["scales"], inp["router_w"],
+                                      inp["router_bias"], x_np)
+        assert np.array_equal(idx.cpu().numpy(), oidx), bi
+        assert gu.ulp_diff_f32(tw.cpu().numpy(), ow).max() <= 1, bi
+        assert gu.rel_err_per_token(got, oref).max() <= 1e-3, bi
     assert int(tier.c.clock) == len(Ts)
     ev.close()
 
@@ -147,8 +155,10 @@ def test_layer_tiered_overlapped_bitidentical(q, wbits, sg, Ts, slots):
 def test_router_lookahead_prefetch_then_layer_bitidentical(q):
     """Layer B's router applied to layer A's input stages B's predicted union while A runs;
     B's tiered call (its input A's plus a small residual update) waits for those copies and
-    equals the resident layer B bit for bit. The prefetch must cover part of B's union."""
+    equals the resident layer B bit for bit, and both layers match the oracle within the
+    1e-3 per-token bar. The prefetch must cover part of B's union."""
     import torch
+    import oracle
     d = gu.dev()
     E, slots, T = 32, 14, 3
     cfgd = dict(hidden=512, ffn=256, n_experts=E, top_k=4, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
@@ -164,7 +174,7 @@ def test_router_lookahead_prefetch_then_layer_bitidentical(q):
         ps = torch.zeros((slots + 1) * nsc, dtype=torch.float32, device=d)
         tier = q.Tier(E, slots)
         q.tier_stage(cfg, slots, hb, hs, [E], [slots], pb, ps)
-        lay.append(dict(res=gu.upload_layer(inp), hb=hb, hs=hs, pb=pb, ps=ps, tier=tier))
+        lay.append(dict(res=gu.upload_layer(inp), hb=hb, hs=hs, pb=pb, ps=ps, tier=tier, inp=inp))
     cs = torch.cuda.Stream(d)
     ev = q.HipEvent()
     ws = q.alloc_tier_workspace(cfg, slots, T, d)
@@ -190,7 +200,12 @@ def test_router_lookahead_prefetch_then_layer_bitidentical(q):
         for l, x_np in ((0, xa_np), (1, xb_np)):
             ref, _, _ = gu.run_layer(cfgd, lay[l]["res"], x_np)
             torch.cuda.synchronize()
-            assert np.array_equal(outs[l].cpu().numpy().view(np.uint32), ref.view(np.uint32)), (bi, l)
+            got = outs[l].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (bi, l)
+            inp = lay[l]["inp"]
+            oref, _, _ = oracle.layer(oracle.make_cfg(**cfgd), inp["blobs"], inp["scales"], inp["router_w"],
+                                      inp["router_bias"], x_np)
+            assert gu.rel_err_per_token(got, oref).max() <= 1e-3, (bi, l)
     ev.close()
     assert prefetched > 0
     print(f"prefetched {prefetched} experts, {later_loads} loaded on demand", flush=True)

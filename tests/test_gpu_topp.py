@@ -1,4 +1,5 @@
-"""Adaptive expert top-p (JustVugg/colibri README, "Useful knobs", --topp) on the HIP
+"""Adaptive expert top-p (the --topp knob of the colibri-strix README, "Experimental resident
+CUDA backend", useful-knobs paragraph) on the HIP
 path against the oracle: the route with its empty slots (index -1, weight 0)
 bit-exact, the grouping of a route with empty slots bit-exact, and the layer and the
 FFN entry point within the parity bar, at decode sizes and past 512 pairs.
