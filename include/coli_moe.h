@@ -90,7 +90,8 @@ typedef enum {
   COLI_E_UNSUPPORTED = -2, /* valid but outside this library's limits (see coli_moe_cfg) */
   COLI_E_WORKSPACE = -3,   /* workspace NULL or smaller than coli_moe_workspace_bytes(cfg, T) */
   COLI_E_ALIGN = -4,       /* a pointer is not aligned as documented */
-  COLI_E_DEVICE = -5       /* the HIP runtime rejected a launch */
+  COLI_E_DEVICE = -5,      /* the HIP runtime rejected a launch */
+  COLI_E_SCRATCH = -6      /* coli_moe_layer_noalloc: the batch needs more than coli_moe_scratch_bytes() */
 } coli_status;
 
 typedef enum { COLI_W_INT2 = 2, COLI_W_INT4 = 4, COLI_W_INT8 = 8, COLI_W_MXFP4 = 40 } coli_wfmt;
@@ -181,6 +182,25 @@ int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float
  * topk_w_opt ([T][k]) receive the route when non-NULL. */
 int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
                    int32_t *topk_idx_opt, float *topk_w_opt, void *workspace, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): coli_moe_layer without a workspace
+ * argument. The work runs on a fixed scratch array that the library holds in device
+ * memory, one per GPU (coli_moe_scratch_bytes() = 32 MiB each, allocated when the library's
+ * code is loaded on that GPU and kept until the process ends); this call allocates
+ * nothing and calls no allocating routine. The scratch belongs to the current device
+ * (hipGetDevice), which must be the device of `stream` and of every pointer argument.
+ * Every call on one GPU uses that GPU's single scratch array: calls that overlap on one
+ * GPU (concurrent streams, or several host threads) race and corrupt each other's
+ * results; serialise them, e.g. on one stream. Nothing in the scratch needs to start at
+ * zero, and the contents left by the previous call are never read.
+ * Returns COLI_E_SCRATCH, with nothing enqueued, when the batch needs more scratch than
+ * that (coli_moe_workspace_bytes(cfg, T) > coli_moe_scratch_bytes(): GLM-5.2-scale decode
+ * fits up to T = 64, OLMoE-scale up to T = 128); otherwise arguments, results and
+ * statuses are those of coli_moe_layer, bit for bit. */
+size_t coli_moe_scratch_bytes(void);
+int coli_moe_layer_noalloc(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                           int32_t *topk_idx_opt, float *topk_w_opt, void *stream);
 
 /* Measurement variant of coli_moe_layer: events[i] (hipEvent_t passed as void*,
  * created by the caller) is recorded on `stream` just before stage i and

@@ -5,8 +5,8 @@ PyTorch supplies device memory and the stream. There is no fallback path: if the
 library is not built, importing any entry point raises.
 
 Entry points (same names as the C ABI in include/coli_moe.h):
-    quantize_q8_0, route, group, ffn, layer, layer_profiled,
-    blob_bytes, workspace_bytes, num_stages, stage_name, strerror;
+    quantize_q8_0, route, group, ffn, layer, layer_noalloc, layer_profiled,
+    blob_bytes, workspace_bytes, scratch_bytes, num_stages, stage_name, strerror;
 plus TimingEvents (HIP events for layer_profiled) and alloc_workspace.
 Tensors must be CUDA tensors, contiguous, with the dtypes documented in the header.
 """
@@ -20,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcolimoe.so")
 
 COLI_OK, COLI_E_INVALID, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_ALIGN, COLI_E_DEVICE = 0, -1, -2, -3, -4, -5
+COLI_E_SCRATCH = -6
 
 
 class ColiError(RuntimeError):
@@ -90,6 +91,9 @@ EXPORTS = {
                                          C.c_void_p, C.c_void_p]),
     "coli_moe_layer": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "coli_moe_scratch_bytes": (C.c_size_t, []),
+    "coli_moe_layer_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p]),
     "coli_moe_layer_profiled": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                           C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p),
                                           C.c_int32]),
@@ -219,6 +223,25 @@ def layer(cfg: Cfg, w: Weights, x, out, workspace, topk_idx=None, topk_w=None, s
     _check(lib().coli_moe_layer(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx),
                                 _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(stream, x)),
            "coli_moe_layer")
+
+
+def scratch_bytes() -> int:
+    """Bytes of the fixed per-GPU scratch that layer_noalloc runs on."""
+    return int(lib().coli_moe_scratch_bytes())
+
+
+def layer_noalloc(cfg: Cfg, w: Weights, x, out, topk_idx=None, topk_w=None, stream=None):
+    """coli_moe_layer_noalloc: the whole layer with no workspace argument, on the library's
+    fixed scratch of the current device (calls on one GPU must not overlap)."""
+    import torch
+    _dt(x, torch.float32, "x"), _dt(out, torch.float32, "out")
+    if topk_idx is not None:
+        _dt(topk_idx, torch.int32, "topk_idx")
+    if topk_w is not None:
+        _dt(topk_w, torch.float32, "topk_w")
+    wc = w.c()
+    _check(lib().coli_moe_layer_noalloc(C.byref(cfg), C.byref(wc), _ptr(x), x.shape[0], _ptr(out), _ptr(topk_idx),
+                                        _ptr(topk_w), _stream(stream, x)), "coli_moe_layer_noalloc")
 
 
 class TimingEvents:

@@ -3,6 +3,8 @@
 // synchronisation, no device allocation).
 #include <limits.h>
 
+#include <mutex>
+
 #include "coli_internal.h"
 #ifdef COLI_TAPS
 #include "../../include/coli_moe_taps.h"
@@ -190,6 +192,33 @@ static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const 
                      ev ? ev + 3 : nullptr, false, tap);
 }
 
+// ---- fixed device scratch of the allocation-free entry point --------------------
+// coli_moe_layer_noalloc runs the same launch sequence as coli_moe_layer on this
+// library-owned array instead of a caller's workspace. It is a file-scope device
+// array (one copy per GPU, allocated when the code object is loaded on that GPU and
+// held until the process ends). In host code `scratch` only names the symbol: its
+// device address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+static int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return COLI_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return COLI_E_DEVICE;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return COLI_OK;
+}
+
 }  // namespace coli
 
 using namespace coli;
@@ -304,6 +333,21 @@ int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const flo
   return layer_impl(cfg, w, x, T, out, topk_idx_opt, topk_w_opt, workspace, ws_bytes, stream, nullptr);
 }
 
+size_t coli_moe_scratch_bytes(void) { return kScratchBytes; }
+
+int coli_moe_layer_noalloc(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
+                           int32_t *topk_idx_opt, float *topk_w_opt, void *stream) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  // the batch must fit the fixed scratch: rejected before anything is enqueued
+  if (coli_moe_workspace_bytes(cfg, T) > kScratchBytes) return COLI_E_SCRATCH;
+  void *ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return layer_impl(cfg, w, x, T, out, topk_idx_opt, topk_w_opt, ws, kScratchBytes, stream, nullptr);
+}
+
 int coli_moe_layer_profiled(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
                             float *out, void *workspace, size_t ws_bytes, void *stream, void **events,
                             int32_t n_events) {
@@ -346,6 +390,7 @@ const char *coli_moe_strerror(int status) {
     case COLI_E_WORKSPACE: return "workspace missing or too small";
     case COLI_E_ALIGN: return "pointer not aligned as required";
     case COLI_E_DEVICE: return "HIP runtime rejected a launch";
+    case COLI_E_SCRATCH: return "batch needs more than the fixed scratch of coli_moe_layer_noalloc";
   }
   return "unknown status";
 }

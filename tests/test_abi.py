@@ -45,7 +45,7 @@ def test_host_queries(q):
     assert q.num_stages() == 7
     assert [q.stage_name(i) for i in range(7)][4] == "ffn_gate_up"
     assert q.stage_name(99) == ""
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert q.strerror(s)
     assert q.strerror(-77) == "unknown status"
 
@@ -173,3 +173,20 @@ def test_taps_library_exports_only_in_test_build():
     for n in names:
         assert not hasattr(prod, n), n
     assert set(taps.TAP_EXPORTS) == set(names)
+
+
+def test_noalloc_rejects_on_the_host(q):
+    """coli_moe_layer_noalloc validates like coli_moe_layer and rejects batches larger than the
+    fixed scratch with COLI_E_SCRATCH, all before anything is enqueued (no GPU needed)."""
+    L = q.lib()
+    assert q.scratch_bytes() == 32 << 20
+    w = _w(q)
+    p = C.c_void_p(FAKE)
+    glm = q.make_cfg(6144, 2048, 256, 8, 8, 4, 2.5, True, 4)
+    assert q.workspace_bytes(glm, 64) <= q.scratch_bytes() < q.workspace_bytes(glm, 128)
+    assert L.coli_moe_layer_noalloc(C.byref(glm), C.byref(w), p, 128, p, None, None, None) == -6
+    assert L.coli_moe_layer_noalloc(C.byref(glm), C.byref(w), p, 0, p, None, None, None) == 0
+    assert L.coli_moe_layer_noalloc(C.byref(glm), C.byref(w), p, -1, p, None, None, None) == -1
+    assert L.coli_moe_layer_noalloc(None, C.byref(w), p, 4, p, None, None, None) == -1
+    bad = q.make_cfg(160, 128, 16, 4)
+    assert L.coli_moe_layer_noalloc(C.byref(bad), C.byref(w), p, 4, p, None, None, None) == -2
