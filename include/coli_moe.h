@@ -272,11 +272,13 @@ size_t coli_moe_tier_workspace_bytes(const coli_moe_cfg *cfg, int32_t slots, int
  * experts' compute (JustVugg/colibri README: missing experts load while resident ones
  * compute):
  *   1. route (w: router_w / router_bias; experts and scales unused) -> route to the host
- *      (this call waits for `stream` here);
- *   2. coli_tier_plan on *tier;
+ *      (this call waits for `stream` here, its only host synchronisation);
+ *   2. coli_tier_plan on *tier; the route is turned into slot ids on the device, by a
+ *      kernel that takes the call's expert -> slot map as an argument;
  *   3. the misses are copied host->HBM on `copy_stream` (a second stream of the same device,
  *      default priority) and `copy_event` is recorded after them;
- *   4. the FFN of the pairs whose experts were resident runs on `stream` meanwhile;
+ *   4. the FFN of the pairs whose experts were resident, the Q8_0 of x and the shared
+ *      expert run on `stream` meanwhile;
  *   5. `stream` waits for `copy_event`, then the FFN of the missing pairs and the combine
  *      over every slot of every token run.
  * The output is bit-identical to coli_moe_layer on the resident weights. The pool
@@ -301,6 +303,12 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
  * that layer's pool on copy_stream, then returns. The layer's next coli_moe_layer_tiered
  * call on the same copy_stream waits for these copies before it reads the pool. Waits for
  * `stream` after the route. workspace: coli_moe_tier_workspace_bytes(cfg, tier->slots, T).
+ * Ordering: the copies overwrite least recently used slots of that pool, so every earlier
+ * call that reads the pool must have finished, or be ordered before copy_stream's next
+ * work, when this is called. A coli_moe_layer_tiered call of a later layer, made on the
+ * same stream as the pool's last tiered call, guarantees it (its route waits for that
+ * stream); otherwise make copy_stream wait for an event recorded after the pool's last
+ * call.
  * *n_loaded_opt receives the number of experts copied. COLI_E_UNSUPPORTED when the
  * predicted union does not fit (nothing copied, *tier unchanged); after COLI_E_DEVICE reset
  * the tier with coli_tier_init. */

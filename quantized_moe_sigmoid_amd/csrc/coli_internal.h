@@ -142,6 +142,21 @@ hipError_t launch_mfma_gateup(int wfmt, const FfnArgs &a, const int4 *tiles, con
                               hipStream_t s);
 hipError_t launch_mfma_down(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
                             hipStream_t s);
+// One phase of coli_moe_ffn for the expert tier (validation as coli_moe_ffn): the Q8_0
+// of x only with quantize_x, the shared expert only with shared, the combine only with
+// combine; the workspace layout is that of cfg. Decode-sized batches group inside the
+// GEMV workgroups from topk_idx (the grouping arrays may then be null).
+int ffn_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, const int32_t *topk_idx,
+              const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm, const int32_t *active,
+              const int32_t *n_active, float *out, void *workspace, size_t ws_bytes, hipStream_t s, bool quantize_x,
+              bool shared, bool combine);
+// coli_moe_route that also quantises x (Q8_0) into xq [T][H] / xd [T][H/32].
+int route_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, int32_t *topk_idx,
+                float *topk_w, void *workspace, size_t ws_bytes, int8_t *xq, float *xd, hipStream_t s);
+// Where a workspace for T tokens holds the Q8_0 of x (the same for every cfg of hidden H).
+int8_t *ws_xq(const coli_moe_cfg &c, int32_t T, void *ws);
+float *ws_xd(const coli_moe_cfg &c, int32_t T, void *ws);
+
 hipError_t launch_combine(const float *ypair, const float *w, int32_t T, int32_t k, int32_t H,
                           int32_t has_shared, float *out, hipStream_t s);
 

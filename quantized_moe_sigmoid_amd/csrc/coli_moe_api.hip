@@ -96,11 +96,14 @@ static Tp *at(void *ws, size_t off) {
 }
 
 // Expert FFNs and combine. With quantize_x the standalone Q8_0 kernel runs first;
-// otherwise x was quantised by the routing kernel.
+// otherwise x was quantised by the routing kernel (or by an earlier phase). Without
+// shared the shared expert's rows are left as they are (an earlier phase computed
+// them); without combine the pair rows are only computed (a later phase combines).
 static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const float *x, int32_t T,
                        const float *topk_w, const int32_t *off, const int32_t *perm, const int32_t *active,
                        const int32_t *nact, const int32_t *local_idx, float *out, void *ws, const WsLayout &L,
-                       hipStream_t s, hipEvent_t *ev, bool quantize_x, float *tap = nullptr) {
+                       hipStream_t s, hipEvent_t *ev, bool quantize_x, float *tap = nullptr, bool shared = true,
+                       bool combine = true) {
   int st;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
   if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), at<float>(ws, L.xd), s))))
@@ -116,7 +119,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.E = c.n_experts;
   a.k = c.top_k;
   a.T = T;
-  a.has_shared = c.has_shared;
+  a.has_shared = shared ? c.has_shared : 0;
   a.off = off;
   a.perm = perm;
   a.active = active;
@@ -140,10 +143,58 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
   if ((st = dev(gemm ? launch_mfma_down(c.wfmt, a, tiles, ntiles, gmax, s) : launch_down(c.wfmt, a, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[3], s)))) return st;
-  if ((st = dev(launch_combine(a.ypair, topk_w, T, c.top_k, c.hidden, c.has_shared, out, s)))) return st;
+  if (combine && (st = dev(launch_combine(a.ypair, topk_w, T, c.top_k, c.hidden, c.has_shared, out, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[4], s)))) return st;
   return COLI_OK;
 }
+
+int ffn_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, const int32_t *topk_idx,
+              const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm, const int32_t *active,
+              const int32_t *n_active, float *out, void *workspace, size_t ws_bytes, hipStream_t s, bool quantize_x,
+              bool shared, bool combine) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if ((st = check_weights(w, true, false))) return st;
+  if (!x || !topk_idx || !topk_w || (combine && !out)) return COLI_E_INVALID;
+  const bool local = (int64_t)T * cfg->top_k <= LOCAL_GROUP_MAX_P;
+  if (!local && (!expert_off || !pair_perm || !active || !n_active)) return COLI_E_INVALID;
+  const WsLayout L = ws_layout(*cfg, T, route_ksplit(*cfg, T));
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  return ffn_enqueue(*cfg, *w, x, T, topk_w, expert_off, pair_perm, active, n_active, local ? topk_idx : nullptr, out,
+                     workspace, L, s, nullptr, quantize_x, nullptr, shared, combine);
+}
+
+int route_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, int32_t *topk_idx,
+                float *topk_w, void *workspace, size_t ws_bytes, int8_t *xq, float *xd, hipStream_t s) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if ((st = check_weights(w, false, true))) return st;
+  if (!x || !topk_idx || !topk_w || !xq || !xd) return COLI_E_INVALID;
+  if (!aligned(x, 16)) return COLI_E_ALIGN;
+  const int32_t ks = route_ksplit(*cfg, T);
+  const WsLayout L = ws_layout(*cfg, T, ks);
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  RouteLaunch r{};
+  r.cfg = cfg;
+  r.x = x;
+  r.T = T;
+  r.W = w->router_w;
+  r.bias = w->router_bias;
+  r.logits = at<double>(workspace, L.logits);
+  r.ksplit = ks;
+  r.idx = topk_idx;
+  r.w = topk_w;
+  r.xq = xq;
+  r.xd = xd;
+  return dev(launch_route(r, s, nullptr));
+}
+
+int8_t *ws_xq(const coli_moe_cfg &c, int32_t T, void *ws) { return at<int8_t>(ws, ws_layout(c, T, 1).xq); }
+float *ws_xd(const coli_moe_cfg &c, int32_t T, void *ws) { return at<float>(ws, ws_layout(c, T, 1).xd); }
 
 // stage order of coli_moe_layer_profiled; a stage fused into the previous kernel is empty
 static const char *const kStages[] = {"route_logits", "route_select", "group", "quantize_x",

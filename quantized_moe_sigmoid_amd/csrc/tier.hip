@@ -9,6 +9,39 @@
 
 #include "coli_internal.h"
 
+namespace {
+
+// Expert -> slot map of one tiered call, passed by value as a kernel argument (the
+// runtime copies arguments at launch, so the host map needs no lifetime beyond the
+// call and no synchronisation): slot of expert e, + TIER_MISS when e is copied in by
+// this call, -1 when e is not in the pool. E <= 1024 and slots <= E.
+constexpr int16_t TIER_MISS = 0x4000;
+struct TierMap {
+  int16_t slot[1024];
+};
+
+// The route in slot ids, split in two halves: s0 the pairs whose expert was resident,
+// s1 (when not null) the pairs whose expert is copied in by this call; the other half
+// holds -1, as does an empty slot (-1) of the route.
+__global__ __launch_bounds__(256) void tier_remap_kernel(const int32_t *__restrict__ idx, int32_t P, TierMap map,
+                                                         int32_t *__restrict__ s0, int32_t *__restrict__ s1) {
+  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < P; p += gridDim.x * blockDim.x) {
+    const int e = idx[p];
+    int a = -1, b = -1;
+    if (e >= 0 && e < 1024) {
+      const int v = map.slot[e];
+      if (v >= 0) {
+        if (v & TIER_MISS) b = v & (TIER_MISS - 1);
+        else a = v;
+      }
+    }
+    s0[p] = a;
+    if (s1) s1[p] = b;
+  }
+}
+
+}  // namespace
+
 extern "C" {
 
 int coli_tier_init(coli_tier *t) {
@@ -190,30 +223,28 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
   const size_t P = (size_t)T * k;
   const size_t a_bytes = L.ffn - L.route, b_bytes = L.idx - L.ffn;
   int st;
-  // 1. route, and the route on the host
-  if ((st = coli_moe_route(cfg, w, x, T, idx, wt, at(L.route), a_bytes, stream))) return st;
-  std::vector<int32_t> hidx(P), hs(P), part[2] = {std::vector<int32_t>(P), std::vector<int32_t>(P)};
+  // 1. route (quantising x into the FFN workspace), and the route on the host (the
+  // call's one host synchronisation)
+  if ((st = coli::route_phase(cfg, w, x, T, idx, wt, at(L.route), a_bytes, coli::ws_xq(pc, T, at(L.ffn)),
+                              coli::ws_xd(pc, T, at(L.ffn)), s)))
+    return st;
+  std::vector<int32_t> hidx(P), hs(P);
   if (hipMemcpyAsync(hidx.data(), idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
   if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;
   // 2. plan
   std::vector<int32_t> le(slots), ls(slots);
   int32_t nl = 0;
   if ((st = coli_tier_plan(tier, hidx.data(), T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
-  // the two halves of the route in slot ids: resident pairs, then the missing pairs
-  std::vector<uint8_t> missing(slots, 0);
-  for (int32_t i = 0; i < nl; i++) missing[ls[i]] = 1;
-  for (size_t p = 0; p < P; p++) {
-    const int32_t v = hs[p];
-    const bool m = v >= 0 && missing[v];
-    part[0][p] = m ? -1 : v;
-    part[1][p] = m ? v : -1;
-  }
+  // the route in slot ids, split into the resident pairs and the missing pairs, on the
+  // device from the call's expert -> slot map
+  TierMap map;
+  for (int32_t e = 0; e < 1024; e++) map.slot[e] = (e < cfg->n_experts) ? (int16_t)tier->slot_of[e] : (int16_t)-1;
+  for (int32_t i = 0; i < nl; i++) map.slot[le[i]] = (int16_t)(ls[i] | TIER_MISS);
   const int nphase = nl > 0 ? 2 : 1;
-  if (nl == 0) part[0] = hs;
-  for (int h = 0; h < nphase; h++)
-    if (hipMemcpyAsync(at(L.sidx[h]), part[h].data(), P * 4, hipMemcpyHostToDevice, s) != hipSuccess)
-      return COLI_E_DEVICE;
-  if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;  // host vectors go out of scope
+  int32_t *sidx0 = static_cast<int32_t *>(at(L.sidx[0])), *sidx1 = static_cast<int32_t *>(at(L.sidx[1]));
+  hipLaunchKernelGGL(tier_remap_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, idx, (int32_t)P, map,
+                     sidx0, nphase == 2 ? sidx1 : nullptr);
+  if (hipGetLastError() != hipSuccess) return COLI_E_DEVICE;
   // 3. copies already enqueued on the copy stream (a lookahead prefetch into this pool: the
   // planner counts their experts as resident) are waited for before the first half; the
   // wait takes the event as recorded here, before this call's own copies are enqueued
@@ -235,10 +266,16 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
     int32_t *cnt = static_cast<int32_t *>(at(L.cnt[h])), *off = static_cast<int32_t *>(at(L.off[h]));
     int32_t *perm = static_cast<int32_t *>(at(L.perm[h])), *act = static_cast<int32_t *>(at(L.act[h]));
     int32_t *nact = static_cast<int32_t *>(at(L.nact[h]));
-    if ((st = coli_moe_group(&pc, si, T, cnt, off, perm, act, nact, stream))) return st;
-    // 4./5. the FFN of this half; its ypair rows stay in the shared FFN workspace, and the
-    // last half's combine sums every slot (the weights of the whole route)
-    if ((st = coli_moe_ffn(&pc, &pw, x, T, si, wt, off, perm, act, nact, out, at(L.ffn), b_bytes, stream)))
+    // batches past the decode size are grouped explicitly; smaller ones group inside the
+    // GEMV workgroups
+    if ((int64_t)T * k > coli::LOCAL_GROUP_MAX_P &&
+        (st = coli_moe_group(&pc, si, T, cnt, off, perm, act, nact, stream)))
+      return st;
+    // 4./5. the FFN of this half. The first runs the shared expert (x was quantised by the
+    // route); the last sums every slot of every token (the weights of the whole route) in
+    // slot order over the pair rows both halves wrote into the shared FFN workspace.
+    if ((st = coli::ffn_phase(&pc, &pw, x, T, si, wt, off, perm, act, nact, out, at(L.ffn), b_bytes, s, false, h == 0,
+                              h == nphase - 1)))
       return st;
   }
   if (topk_idx_opt && hipMemcpyAsync(topk_idx_opt, idx, P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
