@@ -133,15 +133,21 @@ __device__ __forceinline__ float chunk_dot<2>(const uint32_t (&wq)[4], const int
   return r;
 }
 
+// Weight chunks are loaded with the nontemporal hint: each expert row is streamed once
+// per launch, and nontemporal loads stream from HBM faster than cached ones (a plain
+// read of 4 GiB: 7.0 TB/s against 6.3 TB/s; the GLM-scale gate/up GEMV at T = 16: 6.25
+// against 5.85 TB/s).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <int WB>
 __device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<WB>::CHUNK / 4]) {
-  const uint4 a = *reinterpret_cast<const uint4 *>(p);
+  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   wq[0] = a.x;
   wq[1] = a.y;
   wq[2] = a.z;
   wq[3] = a.w;
   if constexpr (Fmt<WB>::CHUNK == 32) {
-    const uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
     wq[4] = b.x;
     wq[5] = b.y;
     wq[6] = b.z;

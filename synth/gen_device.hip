@@ -47,21 +47,32 @@ __global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ d
     dst[g] = src[g];
 }
 
-// Plain streaming read of n16 16-byte words (four loads in flight per thread): the
-// measured read-bandwidth ceiling beside the HBM specification. Each wavefront folds
-// what it read into one word of `sink` ([gridDim.x * 4]), so the loads are not elided.
+// Streaming read of n16 16-byte words: the measured read-bandwidth ceiling beside the
+// HBM specification. Each workgroup reads contiguous chunks of 8 x 256 words (eight
+// 16-byte loads in flight per thread, nontemporal: the data is used once), and each
+// wavefront folds what it read into one word of `sink` ([gridDim.x * 4]) so that the
+// loads are not elided. Words past the last whole chunk are read by a tail loop.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src, int64_t n16,
                                                    uint32_t *__restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int U = 8;
+  const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
+  const int64_t chunk = (int64_t)U * 256;
   uint32_t acc = 0;
-  for (; g + 3 * stride < n16; g += 4 * stride) {
-    const uint4 a = src[g], b = src[g + stride], c = src[g + 2 * stride], d = src[g + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  int64_t base = (int64_t)blockIdx.x * chunk;
+  for (; base + chunk <= n16; base += (int64_t)gridDim.x * chunk) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(s + base + u * 256 + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; g < n16; g += stride) {
-    const uint4 a = src[g];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  // the tail (fewer than gridDim.x * chunk words are left at most; base >= the tail start)
+  for (int64_t g = (n16 / chunk) * chunk + (int64_t)blockIdx.x * 256 + threadIdx.x; g < n16;
+       g += (int64_t)gridDim.x * 256) {
+    const u32x4 v = s[g];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
