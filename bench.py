@@ -281,6 +281,29 @@ def read_bandwidth(mbytes: int, reps: int):
     return n / dt / 1e9
 
 
+def scaled_mfma_ceiling(iters: int = 2000, reps: int = 3):
+    """int8 TOP/s of synth.device.scaled_mfma: v_mfma_i32_32x32x32_i8 with each int32 result
+    converted to fp32 and multiply-added with a scale, in registers only. The rate at which
+    the device can produce exactly scaled Q8_0 block dots: the ceiling of a grouped GEMM
+    that keeps every block dot exact. Median of `reps` launches timed with HIP events on
+    the launch stream."""
+    import torch
+    import synth.device
+    out = synth.device.scaled_mfma_out(torch.device("cuda:0"))
+    synth.device.scaled_mfma(out, 10)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        synth.device.scaled_mfma(out, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    dt = sorted(ts)[len(ts) // 2]
+    return synth.device.scaled_mfma_ops(iters) / dt / 1e12
+
+
 def h2d_bandwidth(mbytes: int = 256, reps: int = 5) -> float:
     """Host->device copy rate from pinned host memory (GB/s): the practical PCIe peak
     beside which the expert tier's copies are measured."""
@@ -624,6 +647,12 @@ def prefill_leg(args, n_calls: int):
     gu_ms, dn_ms = r["stage_ms"][DOMINANT_STAGE], r["stage_ms"]["ffn_down"]
     gops, dops = gateup_ops(wl, T, pairs), down_ops(wl, T, pairs)
     gtops, dtops = gops / (gu_ms * 1e-3) / 1e12, dops / (dn_ms * 1e-3) / 1e12
+    ceil_tops = scaled_mfma_ceiling()
+    log(f"exactly scaled int8 MFMA loop: {ceil_tops:.0f} TOP/s ({ceil_tops / INT8_PEAK_TOPS:.3f} of the int8 peak)")
+    ceiling = {"kernel": "synth scaled_mfma (v_mfma_i32_32x32x32_i8 + v_cvt_f32_i32 + v_fma_f32 per result, "
+                         "registers only)", "TOPs": round(ceil_tops, 1),
+               "frac_of_peak": round(ceil_tops / INT8_PEAK_TOPS, 4),
+               "gate_up_frac_of_ceiling": round(gtops / ceil_tops, 4)}
     layer_tops = (gops + dops) / (r["ms"] * 1e-3) / 1e12
     log(f"prefill T={T}: {r['ms']*1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, U={r['U_mean']:.1f}, gate/up "
         f"{gu_ms*1e3:.1f} us = {gtops:.0f} TOP/s, down {dn_ms*1e3:.1f} us = {dtops:.0f} TOP/s; stages(us) " +
@@ -637,6 +666,7 @@ def prefill_leg(args, n_calls: int):
            "down": {"ops_per_launch": int(dops), "avg_launch_us": round(dn_ms * 1e3, 2),
                     "achieved_TOPs": round(dtops, 1), "frac": round(dtops / INT8_PEAK_TOPS, 4)},
            "layer_TOPs": round(layer_tops, 1), "layer_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
+           "scaled_mfma_ceiling": ceiling,
            "layer_weight_GBps": round(r["layer_weight_gbs"], 1),
            "stage_calls": r["stage_calls"], "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()}}
     del stack
@@ -731,7 +761,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic,
                 "kernel": "mfma_kernel (gate/up grouped GEMM, v_mfma_i32_32x32x32_i8)",
-                "ops_per_launch": ops, "avg_launch_us": round(gu_ms * 1e3, 2)}
+                "ops_per_launch": ops, "avg_launch_us": round(gu_ms * 1e3, 2),
+                "scaled_mfma_ceiling_TOPs": round(scaled_mfma_ceiling(), 1)}
     else:
         ach = head["gateup_gbs"]
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -673,9 +673,121 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
   }
 }
 
+// Software-pipelined form of fast_pass: the wavefront's rows are cut into steps of
+// BR rows x one chunk per lane (8 loads per lane), and the loads of step s + 1 are
+// issued before step s is computed, into a second register set. A wavefront thus
+// keeps its next loads in flight while it computes, instead of waiting one memory
+// round trip per chunk round; the registers held are those of fast_pass (two sets of
+// half the rows). Same products, the same per-lane order of chunks and the same
+// reduce-scatter as fast_pass, so the results are bit-identical.
+template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS>
+__device__ __forceinline__ void fast_pass_pl(const FastCtx &c, int nt, int lane, int wv) {
+  constexpr int RPI = WAVE / LPR;
+  constexpr int CW = Fmt<WB>::CHUNK / 4;
+  constexpr int BPC = Fmt<WB>::BPC;
+  constexpr int LPC = Fmt<WB>::CHUNK / 16;
+  constexpr int TILE = 4 * WR;
+  constexpr int BR_LOAD = cmin<4, (8 / (NMAT * LPC) > 0 ? 8 / (NMAT * LPC) : 1)>::v;
+  constexpr int BR_ACC = (32 / (NMAT * NTC) > 0) ? 32 / (NMAT * NTC) : 1;
+  constexpr int BR_ROWS = (WR / RPI > 0) ? WR / RPI : 1;
+  constexpr int BR = cmin<cmin<BR_LOAD, BR_ACC>::v, BR_ROWS>::v;
+  constexpr int RPB = BR * RPI;  // rows of the wave per batch
+  constexpr int NB = (WR + RPB - 1) / RPB;
+  constexpr int NS = NB * CPL;   // steps: (batch, chunk round)
+  constexpr int V = BR * NMAT * NTC;
+  constexpr int SCAT = cmin<ilog2(V), ilog2(LPR)>::v;
+  constexpr int KEPT = V >> SCAT;
+  constexpr int WMASK = (LPR >> SCAT) - 1;
+  const int rs = lane / LPR, sub = lane % LPR;
+
+  uint32_t w[2][BR][NMAT][CW];
+  float gsr[2][BR][NMAT];  // the chunk's group scale per row (GS)
+  auto row_of = [&](int b, int j) {
+    const int rw = b * RPB + j * RPI + rs;
+    return c.r0 + wv * WR + (rw < WR ? rw : WR - 1);
+  };
+  auto issue = [&](int st, int buf) __attribute__((always_inline)) {
+    const int b = st / CPL, ch = sub + (st % CPL) * LPR;
+#pragma unroll
+    for (int j = 0; j < BR; j++) {
+      const int64_t roff = (int64_t)row_of(b, j) * c.rb + (int64_t)ch * Fmt<WB>::CHUNK;
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? c.mat0 : c.mat1) + roff, w[buf][j][m]);
+      if constexpr (GS) {
+        const int64_t goff = (int64_t)row_of(b, j) * (c.K / GSZ<WB>) + ch * BPC * QK / GSZ<WB>;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) gsr[buf][j][m] = gs_load<WB>(m == 0 ? c.gs0 : c.gs1, goff);
+      }
+    }
+  };
+
+  float acc[V];
+  issue(0, 0);
+#pragma unroll
+  for (int st = 0; st < NS; st++) {
+    const int buf = st & 1, b = st / CPL, ci = st % CPL;
+    if (st + 1 < NS) {
+      // the next step's loads go out before this step's products (kept in this order)
+#pragma unroll
+      for (int j = 0; j < BR; j++)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+          for (int q = 0; q < CW; q++) asm volatile("" : "+v"(w[buf][j][m][q]));
+      issue(st + 1, buf ^ 1);
+    }
+    if (ci == 0) {
+#pragma unroll
+      for (int i = 0; i < V; i++) acc[i] = 0.0f;
+    }
+    const int ch = sub + ci * LPR;
+    Act<WB> act[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; t++)
+      if (t < nt) load_act<WB>(c.xs + t * c.K + ch * BPC * QK, c.xds + t * c.nkb + ch * BPC, act[t]);
+#pragma unroll
+    for (int j = 0; j < BR; j++)
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) {
+        int u[Unp<WB>::N];
+        unpack_chunk<WB>(w[buf][j][m], u);
+#pragma unroll
+        for (int t = 0; t < NTC; t++) {
+          if (t < nt) {
+            if constexpr (GS)
+              acc[(j * NMAT + m) * NTC + t] = fmaf(gsr[buf][j][m], dot_unpacked<WB>(u, act[t]), acc[(j * NMAT + m) * NTC + t]);
+            else
+              acc[(j * NMAT + m) * NTC + t] += dot_unpacked<WB>(u, act[t]);
+          }
+        }
+      }
+    if (ci == CPL - 1) {
+      int base = 0;
+      reduce_scatter<V, LPR / 2>(acc, lane, base);
+      if ((lane & WMASK) == 0) {
+#pragma unroll
+        for (int i = 0; i < KEPT; i++) {
+          const int o = base + i;
+          const int t = o % NTC, m = (o / NTC) % NMAT, j = o / (NTC * NMAT);
+          const int rw = b * RPB + j * RPI + rs;
+          if (t < nt && rw < WR) c.obuf[(m * 8 + t) * TILE + wv * WR + rw] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+// The pipelined pass where it measured faster and fits three wavefronts per SIMD
+// without spilling: int4 gate/up rows of three chunks per lane with one scale per row
+// (GLM-scale experts). Elsewhere its second register set spills or costs occupancy.
+template <int WB, int CPL, int MODE, bool GS>
+struct FastPl {
+  static constexpr bool on = WB == 4 && CPL == 3 && MODE == MODE_GATEUP && !GS;
+};
+
 // GS: one scale per 64 inputs of a row, applied per chunk (see gemv_kernel).
 template <int WB, int LPR, int CPL, int MODE, int WR, bool GS = false>
-__global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
+__global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int TILE = 4 * WR;
   static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
@@ -741,10 +853,17 @@ __global__ __launch_bounds__(256) void gemv_fast_kernel(FfnArgs a, int ntmax) {
       xds[t * nkb + b] = dsrc[(int64_t)orow[8 + t] * nkb + b];
     }
     __syncthreads();
-    if (nt <= 1)
-      fast_pass<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
-    else
-      fast_pass<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
+    if constexpr (FastPl<WB, CPL, MODE, GS>::on) {
+      if (nt <= 1)
+        fast_pass_pl<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
+      else
+        fast_pass_pl<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
+    } else {
+      if (nt <= 1)
+        fast_pass<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
+      else
+        fast_pass<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
+    }
     __syncthreads();
     // epilogue over the tile's rows x nt tokens
     if constexpr (MODE == MODE_GATEUP) {

@@ -22,6 +22,8 @@
 //   select_kernel: one workgroup per token quantises the token's x (Q8_0), sums
 //     the K-split partials in a fixed order (deterministic) and performs the
 //     group-limited top-k as rank computations over LDS.
+#include <type_traits>
+
 #include "q8_0_impl.h"
 
 namespace coli {
@@ -42,6 +44,38 @@ __device__ __forceinline__ double dpp_partner_d(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, 0xF, 0xF, false);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The value that lane l ^ O holds, as a register exchange (no LDS round trip): the
+// permlane swaps for O = 32 and 16, the DPP permutes of dpp_partner_d for O <= 8,
+// whose partners for O = 8 and 4 are l ^ 15 and l ^ 7 (the row mirrors). {1, 2, 7, 15}
+// spans the 16 lanes of a row as {1, 2, 4, 8} does, so a butterfly over O = 1 .. G/2
+// (G a power of two) still combines every lane of each aligned group of G lanes.
+template <int O>
+__device__ __forceinline__ uint32_t partner_u(uint32_t v) {
+  if constexpr (O == 32 || O == 16) {
+    const auto r = (O == 32) ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                             : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & O) ? r[0] : r[1];
+  } else {
+    constexpr int ctrl = (O == 8) ? 0x140 : (O == 4) ? 0x141 : (O == 2) ? 0x4E : 0xB1;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+  }
+}
+
+template <int O>
+__device__ __forceinline__ double partner_d(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = partner_u<O>((uint32_t)b), hi = partner_u<O>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// lane j's value (j wave-uniform), through scalar registers
+__device__ __forceinline__ double lane_d(double v, int j) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
@@ -323,6 +357,36 @@ __device__ __forceinline__ int count_before(const double *val, int lo, int cnt, 
   return r;
 }
 
+// The K-split logit partials of expert e (clamped: every load is valid, values past
+// E or ksplit are never used), first PK of them into registers
+template <int PK>
+__device__ __forceinline__ void load_partials(const SelectArgs &a, int t, int e, double (&pv)[PK]) {
+  const int ec = min(e, a.E - 1);
+#pragma unroll
+  for (int j = 0; j < PK; j++) pv[j] = a.part[((int64_t)min(j, a.ksplit - 1) * a.T + t) * a.E + ec];
+}
+
+// z of expert e: the partials summed in split order (the first PK from registers, the
+// rest loaded eight at a time)
+template <int PK>
+__device__ __forceinline__ double sum_partials(const SelectArgs &a, int t, int e, const double (&pv)[PK]) {
+  double z = 0.0;
+#pragma unroll
+  for (int j = 0; j < PK; j++)
+    if (j < a.ksplit) z += pv[j];
+  const double *pp = a.part + (int64_t)t * a.E + e;
+  const int64_t stride = (int64_t)a.T * a.E;
+  for (int k0 = PK; k0 < a.ksplit; k0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = (k0 + j < a.ksplit) ? pp[(k0 + j) * stride] : 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (k0 + j < a.ksplit) z += v[j];
+  }
+  return z;
+}
+
 // One workgroup per token. Every step is a rank computation over LDS:
 //   c_e in LDS; the rank of e inside its group (c desc, lower index first) gives
 //   the two best values of each group, whose sum is the group score; the rank of a
@@ -356,11 +420,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   constexpr int PK = (EPT == 1) ? 24 : 8;
   double pv[EPT][PK];
 #pragma unroll
-  for (int i = 0; i < EPT; i++) {
-    const int e = min(tid + SEL_NT * i, E - 1);
-#pragma unroll
-    for (int j = 0; j < PK; j++) pv[i][j] = a.part[((int64_t)min(j, a.ksplit - 1) * a.T + t) * E + e];
-  }
+  for (int i = 0; i < EPT; i++) load_partials(a, t, tid + SEL_NT * i, pv[i]);
 
   if (a.xq) {  // eight lanes per 32-value block; XQ blocks per thread loaded at once
     constexpr int XQ = 8;
@@ -398,21 +458,7 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
     s[i] = 0.0;
     c[i] = -INFINITY;
     if (e < E) {
-      // K-split partials summed in split order; loads issued eight at a time
-      double z = 0.0;
-#pragma unroll
-      for (int j = 0; j < PK; j++)
-        if (j < a.ksplit) z += pv[i][j];
-      const double *pp = a.part + (int64_t)t * E + e;
-      const int64_t stride = (int64_t)a.T * E;
-      for (int k0 = PK; k0 < a.ksplit; k0 += 8) {
-        double v[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = (k0 + j < a.ksplit) ? pp[(k0 + j) * stride] : 0.0;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (k0 + j < a.ksplit) z += v[j];
-      }
+      const double z = sum_partials(a, t, e, pv[i]);
       s[i] = 1.0 / (1.0 + exp(-z));
       c[i] = s[i] + (double)a.bias[e];
       cs[e] = c[i];
@@ -501,6 +547,171 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
   }
 }
 
+// Decode-sized batches (x already quantised by the logits kernel) whose experts split
+// evenly over the 64 lanes of a wavefront: E = 64 EPL with EPL in {1, 2, 4, 8}, the
+// EPL experts of a lane inside one group, and a group on a power of two of lanes.
+// The same selection as select_kernel, with the same order (larger value first,
+// lower index on ties) at every step, so the result is identical:
+//   - the workgroup sums each expert's partials and writes s and c to LDS (one
+//     barrier); then a single wavefront works on its registers and lane exchanges:
+//   - a lane sorts its EPL experts; the two best c of a group are merged across the
+//     group's lanes by register exchanges (DPP, permlane swaps), and their sum is the
+//     group score;
+//   - a group is kept when fewer than Gk groups rank before its score;
+//   - the k slots are k rounds of a wavefront arg-max over the lanes' best remaining
+//     kept expert, the winner's lane dropping it: slot r holds the expert of rank r
+//     among the kept experts;
+//   - the weights are formed as in select_kernel (same sums in slot order).
+// Every lane exchange is a register permute (DPP, permlane swap) or a readlane: the
+// k arg-max rounds form a chain of 6 k dependent exchanges, which as LDS-routed
+// shuffles cost about 3.5 us at k = 8 and as register permutes a fraction of that.
+template <int EPL>
+__global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a) {
+  constexpr int E = 64 * EPL;
+  constexpr int EPT = (E + SEL_NT - 1) / SEL_NT;
+  constexpr int PK = (EPT == 1) ? 24 : 12;
+  __shared__ double cs[E], ss[E];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  double pv[EPT][PK];
+#pragma unroll
+  for (int i = 0; i < EPT; i++) load_partials(a, t, tid + SEL_NT * i, pv[i]);
+#pragma unroll
+  for (int i = 0; i < EPT; i++) {
+    const int e = tid + SEL_NT * i;
+    if (e < E) {
+      const double z = sum_partials(a, t, e, pv[i]);
+      const double sv = 1.0 / (1.0 + exp(-z));
+      ss[e] = sv;
+      cs[e] = sv + (double)a.bias[e];
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid, G = a.G, k = a.k;
+  const int m = E / G;        // experts per group
+  const int lpg = m / EPL;    // lanes per group
+  double v[EPL];
+  int id[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; i++) {
+    id[i] = EPL * lane + i;
+    v[i] = cs[id[i]];
+  }
+  // the lane's experts, best first
+#pragma unroll
+  for (int p = 0; p + 1 < EPL; p++)
+#pragma unroll
+    for (int q = 0; q + 1 < EPL - p; q++)
+      if (before(v[q + 1], id[q + 1], v[q], id[q])) {
+        const double tv = v[q];
+        v[q] = v[q + 1];
+        v[q + 1] = tv;
+        const int ti = id[q];
+        id[q] = id[q + 1];
+        id[q + 1] = ti;
+      }
+  bool kept = true;
+  if (G > 1) {
+    // the group's two largest c on every lane of the group
+    double t1 = v[0], t2 = (EPL > 1) ? v[1] : -INFINITY;
+    auto merge = [&](auto o_tag) __attribute__((always_inline)) {
+      constexpr int O = decltype(o_tag)::value;
+      const double b1 = partner_d<O>(t1), b2 = partner_d<O>(t2);
+      const double lo = (b1 > t1) ? t1 : b1;
+      const double hi2 = (b2 > t2) ? b2 : t2;
+      t1 = (b1 > t1) ? b1 : t1;
+      t2 = (hi2 > lo) ? hi2 : lo;
+    };
+    if (lpg > 1) merge(std::integral_constant<int, 1>{});
+    if (lpg > 2) merge(std::integral_constant<int, 2>{});
+    if (lpg > 4) merge(std::integral_constant<int, 4>{});
+    if (lpg > 8) merge(std::integral_constant<int, 8>{});
+    if (lpg > 16) merge(std::integral_constant<int, 16>{});
+    if (lpg > 32) merge(std::integral_constant<int, 32>{});
+    const double score = (m > 1) ? t1 + t2 : t1;
+    const int g = lane / lpg;
+    int rank = 0;
+    for (int j = 0; j < G; j++) rank += before(lane_d(score, j * lpg), j, score, g) ? 1 : 0;
+    kept = rank < a.Gk;
+  }
+  if (!kept) {
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+      v[i] = -INFINITY;
+      id[i] = INT_MAX;
+    }
+  }
+  int my_e = -1;
+  for (int r = 0; r < k; r++) {
+    double bv = v[0];
+    int bi = id[0];
+    auto step = [&](auto o_tag) __attribute__((always_inline)) {
+      constexpr int O = decltype(o_tag)::value;
+      const double ov = partner_d<O>(bv);
+      const int oi = (int)partner_u<O>((uint32_t)bi);
+      if (before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    };
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 8>{});
+    step(std::integral_constant<int, 16>{});
+    step(std::integral_constant<int, 32>{});
+    if (lane == r) my_e = bi;
+    if (id[0] == bi) {  // this lane's best was taken
+#pragma unroll
+      for (int i = 0; i + 1 < EPL; i++) {
+        v[i] = v[i + 1];
+        id[i] = id[i + 1];
+      }
+      v[EPL - 1] = -INFINITY;
+      id[EPL - 1] = INT_MAX;
+    }
+  }
+  const double s_me = (lane < k) ? ss[my_e] : 0.0;
+  double S = 0.0;
+  for (int j = 0; j < k; j++) S += lane_d(s_me, j);
+  int kept_n = k;
+  if (a.topp > 0.0f) {
+    // adaptive top-p, as in select_kernel
+    const double target = (double)a.topp * S;
+    double cum = 0.0;
+    for (int j = 0; j < k; j++) {
+      cum += lane_d(s_me, j);
+      if (cum >= target) {
+        kept_n = j + 1;
+        break;
+      }
+    }
+    S = cum;
+  }
+  if (lane < k) {
+    int e = my_e;
+    float wt = (float)((s_me / S) * (double)a.rsf);
+    if (lane >= kept_n) {
+      e = -1;
+      wt = 0.0f;
+    }
+    a.idx[(int64_t)t * k + lane] = e;
+    a.w[(int64_t)t * k + lane] = wt;
+  }
+}
+
+// select_wave_kernel's layout conditions; returns its EPL or 0
+static int wave_select_epl(int E, int G, bool x_done) {
+  if (!x_done || E % 64 || E > 512 || G <= 0 || E % G) return 0;
+  const int epl = E / 64;
+  if (epl & (epl - 1)) return 0;
+  const int m = E / G;
+  if (m % epl) return 0;
+  const int lpg = m / epl;
+  if (lpg & (lpg - 1)) return 0;
+  return epl;
+}
+
 // ------------------------------------------------------------------ host side
 int32_t route_ksplit(const coli_moe_cfg &c, int32_t T) {
   if (T <= LD_TT && c.hidden % 256 == 0) return c.hidden / 256;  // 256-wide K chunks: enough workgroups at decode sizes
@@ -555,6 +766,13 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.xq = x_done ? nullptr : r.xq;
   a.xd = r.xd;
   if (T == 0) return hipSuccess;
+  switch (wave_select_epl(E, c.n_group, x_done)) {
+    case 1: hipLaunchKernelGGL(select_wave_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
+    case 2: hipLaunchKernelGGL(select_wave_kernel<2>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
+    case 4: hipLaunchKernelGGL(select_wave_kernel<4>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
+    case 8: hipLaunchKernelGGL(select_wave_kernel<8>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
+    default: break;
+  }
   if (E <= SEL_NT)
     hipLaunchKernelGGL(select_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a);
   else if (E <= 2 * SEL_NT)

@@ -39,6 +39,11 @@ def lib():
         L.coli_synth_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
         L.coli_synth_read.restype = C.c_int
         L.coli_synth_read_sink_words.restype = C.c_int
+        L.coli_synth_scaled_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_void_p]
+        L.coli_synth_scaled_mfma.restype = C.c_int
+        L.coli_synth_scaled_mfma_out_words.restype = C.c_int
+        L.coli_synth_scaled_mfma_ops.argtypes = [C.c_int32]
+        L.coli_synth_scaled_mfma_ops.restype = C.c_double
         _lib = L
     return _lib
 
@@ -94,3 +99,27 @@ def read(src, sink, stream=None):
                                C.c_void_p(s.cuda_stream))
     if rc != 0:
         raise RuntimeError(f"coli_synth_read failed: {rc}")
+
+
+def scaled_mfma_out(device):
+    """A device buffer for scaled_mfma()'s per-thread results."""
+    import torch
+    return torch.empty(lib().coli_synth_scaled_mfma_out_words(), dtype=torch.float32, device=device)
+
+
+def scaled_mfma_ops(iters: int) -> float:
+    """int8 operations of one scaled_mfma launch."""
+    return float(lib().coli_synth_scaled_mfma_ops(iters))
+
+
+def scaled_mfma(out, iters: int, stream=None):
+    """int8 matrix-core loop with every block dot converted to fp32 and multiply-added
+    with a scale: the device's rate for exactly scaled Q8_0 block dots."""
+    import torch
+
+    assert out.is_cuda and out.dtype == torch.float32
+    assert out.numel() >= lib().coli_synth_scaled_mfma_out_words()
+    s = stream if stream is not None else torch.cuda.current_stream(out.device)
+    rc = lib().coli_synth_scaled_mfma(C.c_void_p(out.data_ptr()), iters, C.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"coli_synth_scaled_mfma failed: {rc}")

@@ -1,7 +1,9 @@
 // gen_device.hip — device-side twin of synth.expert_blob(): fills packed expert
 // blobs with the SplitMix64 stream of each expert's key. Integer arithmetic only,
 // so the bytes equal the host generator's bit for bit. Not part of the MoE
-// library: it only produces synthetic inputs.
+// library: it produces synthetic inputs, plus the reference kernels that the
+// benchmark times beside the library's (a copy and a streaming read of known
+// traffic, and an exactly scaled int8 matrix-core loop).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,6 +81,48 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
 }
 
+// Throughput of int8 matrix-core work that scales every block dot exactly: a loop of
+// v_mfma_i32_32x32x32_i8 (32 rows x 32 columns x one 32-value block) whose 16 int32
+// results per lane are each converted to fp32 and multiply-added into an fp32
+// accumulator with a per-lane factor, with no memory traffic in the loop. That is the
+// arithmetic a grouped GEMM over Q8_0 blocks performs per block when it keeps each
+// block dot exact and applies the block's scale to it, so the measured rate is that
+// GEMM's ceiling on the device, beside the 5.0 POP/s int8 specification (which
+// counts the matrix cores alone). Two independent chains per wavefront; the operands
+// change every iteration, so nothing is loop-invariant.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int v16i_t __attribute__((ext_vector_type(16)));
+
+constexpr int kMfGrid = 2048;  // 8 workgroups of 4 wavefronts per CU on 256 CUs
+
+__global__ __launch_bounds__(256) void scaled_mfma_kernel(float *__restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  v4i_t a = {lane, 3 * lane + 1, 5, 7}, b = {11 - lane, 13, 2 * lane + 17, 19};
+  const float d0 = 1.0e-3f * (float)(lane + 1), d1 = 2.0e-3f * (float)(lane + 2);
+  float acc0[16], acc1[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    acc0[r] = 0.0f;
+    acc1[r] = 0.0f;
+  }
+  for (int i = 0; i < iters; i++) {
+    const v16i_t z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const v16i_t I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+    const v16i_t I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, z, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      acc0[r] = fmaf(d0, (float)I0[r], acc0[r]);
+      acc1[r] = fmaf(d1, (float)I1[r], acc1[r]);
+    }
+    a.x += 1;
+    b.z += 1;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) s += acc0[r] + acc1[r];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 constexpr int kReadGrid = 4096;
@@ -109,5 +153,20 @@ extern "C" int coli_synth_fill_blobs(void *out, const void *keys_dev, int64_t bl
   hipLaunchKernelGGL(fill_blobs_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<uint64_t *>(out), static_cast<const uint64_t *>(keys_dev), words, n_blobs,
                      wbits == 8 ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int coli_synth_scaled_mfma_out_words(void) { return kMfGrid * 256; }
+
+// int8 operations (2 per multiply-add) of one coli_synth_scaled_mfma launch
+extern "C" double coli_synth_scaled_mfma_ops(int32_t iters) {
+  return 2.0 * 32 * 32 * 32 * 2 /* MFMAs per iteration */ * (double)iters * 4 /* wavefronts */ * kMfGrid;
+}
+
+extern "C" int coli_synth_scaled_mfma(void *out, int32_t iters, void *stream) {
+  if (!out || iters <= 0) return -1;
+  if (((uintptr_t)out % 4) != 0) return -4;
+  hipLaunchKernelGGL(scaled_mfma_kernel, dim3(kMfGrid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<float *>(out), iters);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

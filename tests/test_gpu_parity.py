@@ -131,6 +131,68 @@ def test_route_ties_lowest_index(q, orc):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
+# The wavefront selection kernel serves batches of up to 16 tokens with H a multiple of
+# 256 and E = 64 EPL (EPL 1, 2, 4, 8), a lane's experts in one group and a group on a
+# power of two of lanes. Every layout it handles, against the oracle.
+WAVE_CASES = [  # E, G, Gk, k, T, topp
+    (64, 1, 1, 8, 3, 0.0),        # one group
+    (64, 64, 8, 4, 5, 0.0),       # one expert per group: the group score is c itself
+    (64, 8, 3, 6, 16, 0.0),       # one expert per lane, 8 lanes per group
+    (128, 4, 2, 8, 7, 0.0),       # two experts per lane, 16 lanes per group
+    (128, 64, 10, 12, 2, 0.0),    # two experts per lane, one lane per group
+    (128, 2, 1, 8, 4, 0.0),       # two experts per lane, 32 lanes per group
+    (256, 8, 4, 8, 16, 0.0),      # GLM-scale router
+    (256, 1, 1, 64, 4, 0.0),      # k = 64: every lane holds a slot
+    (512, 8, 4, 8, 9, 0.0),       # eight experts per lane
+    (512, 64, 16, 16, 1, 0.0),    # eight experts per lane, one lane per group
+    (256, 8, 4, 8, 16, 0.7),      # adaptive top-p
+]
+
+
+def _route_both(q, orc, cfgd, inp, T):
+    import torch
+    w = q.Weights(None, None, gu.to_dev(inp["router_w"]), gu.to_dev(inp["router_bias"]))
+    cfg = q.make_cfg(**cfgd)
+    k = cfgd["top_k"]
+    idx = torch.empty((T, k), dtype=torch.int32, device=gu.dev())
+    tw = torch.empty((T, k), dtype=torch.float32, device=gu.dev())
+    q.route(cfg, w, gu.to_dev(inp["x"]), idx, tw, q.alloc_workspace(cfg, T, gu.dev()))
+    torch.cuda.synchronize()
+    ridx, rw = orc.route(orc.make_cfg(**cfgd), inp["router_w"], inp["router_bias"], inp["x"])
+    return idx.cpu().numpy(), tw.cpu().numpy(), ridx, rw
+
+
+@pytest.mark.parametrize("E,G,Gk,k,T,topp", WAVE_CASES)
+def test_route_wave_select_bitexact(q, orc, E, G, Gk, k, T, topp):
+    cfgd = _cfg(hidden=256, n_experts=E, top_k=k, n_group=G, topk_group=Gk, rsf=2.5, topp=topp)
+    inp = synth.layer_inputs(300 + E + G + k + T, 0, tokens=T, hidden=256, ffn=128, n_experts=E, has_shared=False,
+                             wbits=4, with_blobs=False)
+    idx, tw, ridx, rw = _route_both(q, orc, cfgd, inp, T)
+    assert np.array_equal(idx, ridx)
+    assert gu.ulp_diff_f32(tw, rw).max() <= 1
+    if topp > 0:
+        assert (ridx < 0).any()  # the top-p cut removed slots in this batch
+
+
+def test_route_wave_select_ties(q, orc):
+    """Exact ties on the wavefront path: experts with identical router rows and equal bias,
+    inside one group and across groups, and two groups identical as a whole (equal group
+    scores): the lower index wins every tie, as in the oracle."""
+    E, G = 128, 4
+    cfgd = _cfg(hidden=256, n_experts=E, top_k=8, n_group=G, topk_group=2, rsf=2.5)
+    T = 16
+    inp = synth.layer_inputs(77, 0, tokens=T, hidden=256, ffn=128, n_experts=E, has_shared=False, wbits=4,
+                             with_blobs=False)
+    rw, rb = inp["router_w"], inp["router_bias"]
+    rb[:] = 0.0
+    for e in (5, 17, 70):
+        rw[e] = rw[2]
+    rw[96:128] = rw[32:64]   # group 3 equals group 1
+    idx, tw, ridx, rwt = _route_both(q, orc, cfgd, inp, T)
+    assert np.array_equal(idx, ridx)
+    assert gu.ulp_diff_f32(tw, rwt).max() <= 1
+
+
 # ---------------------------------------------------------------- group
 @pytest.mark.parametrize("E,k,T,zipf", [(16, 4, 8, False), (64, 8, 16, False), (256, 8, 2048, True),
                                         (256, 8, 1, False), (8, 8, 5, False), (1024, 8, 300, True),
