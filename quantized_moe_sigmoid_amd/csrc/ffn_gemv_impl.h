@@ -160,8 +160,37 @@ __device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<
 // kept separately so that one unpack serves every token.
 template <int WB>
 struct Unp {
-  static constexpr int N = (WB == 2) ? 16 : 8;  // dwords of unpacked weights per chunk
+  // dwords of unpacked weights per chunk (MXFP4: 16 dwords of fp16 pairs)
+  static constexpr int N = (WB == 2 || WB == W_MX) ? 16 : 8;
 };
+
+// MXFP4 in the batched and pipelined GEMVs: the E2M1 codes are converted to fp16 by
+// the hardware (v_cvt_scalef32_pk_f16_fp4, scale 1: byte b of a dword gives the pair
+// (low nibble, high nibble) = (K_j, K_j+16), j = 4 i + b in dword i of the chunk), the
+// Q8_0 codes to fp16 pairs (q_j, q_j+16) once per token and chunk, and v_dot2_f32_f16
+// sums the products. Every E2M1 value (0 .. 6 in halves) and every code (|q| <= 127) is
+// exact in fp16, each product is exact in fp32 and every partial sum of a block is a
+// multiple of 1/2 below 2^15, so the fp32 sum is the block's exact J_b = sum e2m1 * q,
+// the same number as the integer path's 2 * J_b / 2.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 32 Q8_0 codes of a block (x[i] = codes 4 i .. 4 i + 3) -> 16 fp16 pairs (q_j, q_j+16):
+// a byte permute places q_j and q_j+16 over zero bytes, an XOR turns each half into
+// 0x64 : (q + 128), the fp16 number 1024 + q + 128, and one packed fp16 subtraction of
+// 1152 leaves q exactly.
+__device__ __forceinline__ void q8_to_f16_pairs(const int (&x)[8], uint32_t (&h)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
+      const uint32_t t = __builtin_amdgcn_perm((uint32_t)x[4 + i], (uint32_t)x[i], sel) ^ 0x64806480u;
+      h[4 * i + b] = as_u32(as_f16x2(t) - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
+    }
+}
 
 template <int WB>
 __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK / 4], int (&u)[Unp<WB>::N]) {
@@ -177,8 +206,10 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK
   } else if constexpr (WB == W_MX) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      u[i] = (int)e2m1x4_to_i8x4(wq[i]);
-      u[4 + i] = (int)e2m1x4_to_i8x4(wq[i] >> 4);
+      u[4 * i] = (int)as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[i], 1.0f, 0));
+      u[4 * i + 1] = (int)as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[i], 1.0f, 1));
+      u[4 * i + 2] = (int)as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[i], 1.0f, 2));
+      u[4 * i + 3] = (int)as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[i], 1.0f, 3));
     }
   } else {
     // block blk, element dword d (elements 4d..4d+3) = field m of source dword h, d = 2m + h
@@ -193,7 +224,8 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK
   }
 }
 
-// activation registers of one chunk for one token: Q8_0 bytes and d per block
+// activation registers of one chunk for one token: Q8_0 bytes (MXFP4: fp16 pairs) and
+// d per block
 template <int WB>
 struct Act {
   int x[Unp<WB>::N];
@@ -202,13 +234,29 @@ struct Act {
 
 template <int WB>
 __device__ __forceinline__ void load_act(const int8_t *xa, const float *xd, Act<WB> &a) {
+  if constexpr (WB == W_MX) {
+    int q[8];
 #pragma unroll
-  for (int i = 0; i < Unp<WB>::N / 4; i++) {
-    const int4 v = *reinterpret_cast<const int4 *>(xa + 16 * i);
-    a.x[4 * i] = v.x;
-    a.x[4 * i + 1] = v.y;
-    a.x[4 * i + 2] = v.z;
-    a.x[4 * i + 3] = v.w;
+    for (int i = 0; i < 2; i++) {
+      const int4 v = *reinterpret_cast<const int4 *>(xa + 16 * i);
+      q[4 * i] = v.x;
+      q[4 * i + 1] = v.y;
+      q[4 * i + 2] = v.z;
+      q[4 * i + 3] = v.w;
+    }
+    uint32_t h[16];
+    q8_to_f16_pairs(q, h);
+#pragma unroll
+    for (int j = 0; j < 16; j++) a.x[j] = (int)h[j];
+  } else {
+#pragma unroll
+    for (int i = 0; i < Unp<WB>::N / 4; i++) {
+      const int4 v = *reinterpret_cast<const int4 *>(xa + 16 * i);
+      a.x[4 * i] = v.x;
+      a.x[4 * i + 1] = v.y;
+      a.x[4 * i + 2] = v.z;
+      a.x[4 * i + 3] = v.w;
+    }
   }
 #pragma unroll
   for (int b = 0; b < Fmt<WB>::BPC; b++) a.d[b] = xd[b];
@@ -216,6 +264,12 @@ __device__ __forceinline__ void load_act(const int8_t *xa, const float *xd, Act<
 
 template <int WB>
 __device__ __forceinline__ float dot_unpacked(const int (&u)[Unp<WB>::N], const Act<WB> &a) {
+  if constexpr (WB == W_MX) {
+    float j = 0.0f;  // J_b, exact
+#pragma unroll
+    for (int i = 0; i < 16; i++) j = __builtin_amdgcn_fdot2(as_f16x2((uint32_t)u[i]), as_f16x2((uint32_t)a.x[i]), j, false);
+    return a.d[0] * (2.0f * j);  // 2 J_b, as the integer path (INV = 1/2 at the end)
+  }
   float r = 0.0f;
 #pragma unroll
   for (int b = 0; b < Fmt<WB>::BPC; b++) {
