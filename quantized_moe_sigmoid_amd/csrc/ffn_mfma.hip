@@ -375,6 +375,37 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
       v4i A[NMAT][2];
 #pragma unroll
       for (int m = 0; m < NMAT; m++) a_pair<WB>(st[m], jp, A[m]);
+      if constexpr (GS && G == 2 * QK && WB != 2) {
+        // 64-input groups: the pair's blocks 2 jp and 2 jp + 1 share group jp's scale, so
+        // each result takes g * (d0 * I0 + d1 * I1), the group sum of the definition
+        // (five VALU operations per two blocks instead of six)
+#pragma unroll
+        for (int t = 0; t < GM_TILES; t++) {
+          if (t >= nt) continue;
+          const v4i bv0 = *reinterpret_cast<const v4i *>(&L.x[buf][32 * t + li][2 * jp * QK + 16 * h]);
+          const v4i bv1 = *reinterpret_cast<const v4i *>(&L.x[buf][32 * t + li][(2 * jp + 1) * QK + 16 * h]);
+          const float d0 = L.d[buf][32 * t + li][2 * jp], d1 = L.d[buf][32 * t + li][2 * jp + 1];
+#pragma unroll
+          for (int m = 0; m < NMAT; m++) {
+            const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            const v16i I0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[m][0], bv0, zero, 0, 0, 0);
+            const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[m][1], bv1, zero, 0, 0, 0);
+            const float *gr = &L.gs[buf][m][jp][32 * wv + 4 * h];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const float4 g4 = *reinterpret_cast<const float4 *>(gr + 8 * q);
+              const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+              for (int c = 0; c < 4; c++) {
+                const int r = 4 * q + c;
+                const float sum = fmaf(d1, (float)I1[r], d0 * (float)I0[r]);
+                acc[m][t][r] = fmaf(gq[c], sum, acc[m][t][r]);
+              }
+            }
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 2; i++) {
         const int kb = pair_block<WB>(jp, i);
