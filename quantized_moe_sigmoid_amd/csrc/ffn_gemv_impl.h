@@ -139,15 +139,18 @@ __device__ __forceinline__ float chunk_dot<2>(const uint32_t (&wq)[4], const int
 // against 5.85 TB/s).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int WB>
+// KEEP: an ordinary (L2-allocating) load, for rows that are read again by later token
+// passes of the same workgroup.
+template <int WB, bool KEEP = false>
 __device__ __forceinline__ void load_chunk(const uint8_t *p, uint32_t (&wq)[Fmt<WB>::CHUNK / 4]) {
-  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  const u32x4 a = KEEP ? *reinterpret_cast<const u32x4 *>(p) : __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   wq[0] = a.x;
   wq[1] = a.y;
   wq[2] = a.z;
   wq[3] = a.w;
   if constexpr (Fmt<WB>::CHUNK == 32) {
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
+    const u32x4 b = KEEP ? *reinterpret_cast<const u32x4 *>(p + 16)
+                         : __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
     wq[4] = b.x;
     wq[5] = b.y;
     wq[6] = b.z;
@@ -643,7 +646,7 @@ struct FastCtx {
   const void *gs0, *gs1;  // group scales [rows][K/G] of the two matrices (GS only; see gs_base)
 };
 
-template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS>
+template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS, bool KEEP = false>
 __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, int wv) {
   constexpr int RPI = WAVE / LPR;
   constexpr int CW = Fmt<WB>::CHUNK / 4;
@@ -683,7 +686,7 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
       for (int j = 0; j < BR; j++)
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
-          load_chunk<WB>((m == 0 ? c.mat0 : c.mat1) + roff[j] + (int64_t)ch * Fmt<WB>::CHUNK, w[j][m]);
+          load_chunk<WB, KEEP>((m == 0 ? c.mat0 : c.mat1) + roff[j] + (int64_t)ch * Fmt<WB>::CHUNK, w[j][m]);
       float gsr[BR][NMAT];  // the chunk's group scale per row (a chunk lies in one group)
       if constexpr (GS) {
 #pragma unroll
@@ -734,7 +737,7 @@ __device__ __forceinline__ void fast_pass(const FastCtx &c, int nt, int lane, in
 // round trip per chunk round; the registers held are those of fast_pass (two sets of
 // half the rows). Same products, the same per-lane order of chunks and the same
 // reduce-scatter as fast_pass, so the results are bit-identical.
-template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS>
+template <int WB, int NMAT, int LPR, int CPL, int WR, int NTC, bool GS, bool KEEP = false>
 __device__ __forceinline__ void fast_pass_pl(const FastCtx &c, int nt, int lane, int wv) {
   constexpr int RPI = WAVE / LPR;
   constexpr int CW = Fmt<WB>::CHUNK / 4;
@@ -766,7 +769,7 @@ __device__ __forceinline__ void fast_pass_pl(const FastCtx &c, int nt, int lane,
     for (int j = 0; j < BR; j++) {
       const int64_t roff = (int64_t)row_of(b, j) * c.rb + (int64_t)ch * Fmt<WB>::CHUNK;
 #pragma unroll
-      for (int m = 0; m < NMAT; m++) load_chunk<WB>((m == 0 ? c.mat0 : c.mat1) + roff, w[buf][j][m]);
+      for (int m = 0; m < NMAT; m++) load_chunk<WB, KEEP>((m == 0 ? c.mat0 : c.mat1) + roff, w[buf][j][m]);
       if constexpr (GS) {
         const int64_t goff = (int64_t)row_of(b, j) * (c.K / GSZ<WB>) + ch * BPC * QK / GSZ<WB>;
 #pragma unroll
@@ -907,13 +910,20 @@ __global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void 
       xds[t * nkb + b] = dsrc[(int64_t)orow[8 + t] * nkb + b];
     }
     __syncthreads();
+    // a slot with more tokens than one pass takes re-reads its rows on every pass: those
+    // loads allocate in L2 so that the later passes find them there
+    const bool keep = n > ntmax;
     if constexpr (FastPl<WB, CPL, MODE, GS>::on) {
-      if (nt <= 1)
+      if (keep)
+        fast_pass_pl<WB, NMAT, LPR, CPL, WR, 2, GS, true>(c, nt, lane, wv);
+      else if (nt <= 1)
         fast_pass_pl<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
       else
         fast_pass_pl<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
     } else {
-      if (nt <= 1)
+      if (keep)
+        fast_pass<WB, NMAT, LPR, CPL, WR, 2, GS, true>(c, nt, lane, wv);
+      else if (nt <= 1)
         fast_pass<WB, NMAT, LPR, CPL, WR, 1, GS>(c, nt, lane, wv);
       else
         fast_pass<WB, NMAT, LPR, CPL, WR, 2, GS>(c, nt, lane, wv);
