@@ -271,26 +271,28 @@ size_t coli_moe_tier_workspace_bytes(const coli_moe_cfg *cfg, int32_t slots, int
 /* One layer through the tier, on `stream`, with the misses' loads overlapping the resident
  * experts' compute (JustVugg/colibri README: missing experts load while resident ones
  * compute):
- *   1. route (w: router_w / router_bias; experts and scales unused) -> route to the host
- *      (this call waits for `stream` here, its only host synchronisation);
- *   2. coli_tier_plan on *tier; the route is turned into slot ids on the device, by a
- *      kernel that takes the call's expert -> slot map as an argument;
- *   3. the misses are copied host->HBM on `copy_stream` (a second stream of the same device,
- *      default priority) and `copy_event` is recorded after them;
- *   4. the FFN of the pairs whose experts were resident, the Q8_0 of x and the shared
- *      expert run on `stream` meanwhile;
- *   5. `stream` waits for `copy_event`, then the FFN of the missing pairs and the combine
- *      over every slot of every token run.
+ *   1. route (w: router_w / router_bias; experts and scales unused);
+ *   2. on the device, the route in slot ids of the experts the pool holds when the call
+ *      starts (a kernel that takes that expert -> slot map as an argument; the pairs of
+ *      experts not in the pool get -1), and the route into pinned host memory;
+ *   3. the FFN of those resident pairs, the shared expert among them, is enqueued at once;
+ *   4. the call waits for the route (an event recorded after step 2, its only wait for the
+ *      device; the FFN of step 3 keeps running) and runs coli_tier_plan on *tier;
+ *   5. the misses are copied host->HBM on `copy_stream` (a second stream of the same device,
+ *      default priority) and `copy_event` is recorded after them; `stream` waits for it,
+ *      then the FFN of the missing pairs and the combine over every slot of every token run
+ *      (with no misses, the combine alone).
  * The output is bit-identical to coli_moe_layer on the resident weights. The pool
  * (pool_experts / pool_scales: slots + has_shared entries) must already hold the shared
  * expert in slot `slots` (coli_moe_tier_stage with load_expert = E). host_experts /
  * host_scales: all E + has_shared experts in pinned host memory. topk_idx_opt / topk_w_opt
- * (device, [T][k]) receive the route (expert ids) when non-NULL. With no misses the whole
- * FFN runs once, as in coli_moe_layer. COLI_E_UNSUPPORTED when the union does not fit
- * (nothing is copied or computed after the route; *tier is unchanged). After COLI_E_DEVICE
- * the tier may list experts whose copies did not run: reset it with coli_tier_init. The
- * tier's arrays and the host experts must stay valid until `stream` and `copy_stream` have
- * run the call. */
+ * (device, [T][k]) receive the route (expert ids) when non-NULL. COLI_E_UNSUPPORTED when the
+ * union does not fit: nothing is copied, `out` is not written and *tier is unchanged (the
+ * resident pairs' FFN of step 3 has run into the workspace). After COLI_E_DEVICE the tier
+ * may list experts whose copies did not run: reset it with coli_tier_init. The tier's
+ * arrays and the host experts must stay valid until `stream` and `copy_stream` have run the
+ * call. The library keeps one pinned host buffer for the route and one event per device for
+ * each calling host thread; calls from one thread are sequential. */
 int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, coli_tier *tier,
                           const void *host_experts, const void *host_scales, void *pool_experts, void *pool_scales,
                           const float *x, int32_t T, float *out, int32_t *topk_idx_opt, float *topk_w_opt,

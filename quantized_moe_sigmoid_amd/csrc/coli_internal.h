@@ -150,6 +150,9 @@ int ffn_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x
               const float *topk_w, const int32_t *expert_off, const int32_t *pair_perm, const int32_t *active,
               const int32_t *n_active, float *out, void *workspace, size_t ws_bytes, hipStream_t s, bool quantize_x,
               bool shared, bool combine);
+// The combine of ffn_phase alone (the pair rows of earlier phases, workspace layout of cfg).
+int combine_phase(const coli_moe_cfg *cfg, int32_t T, const float *topk_w, float *out, void *workspace,
+                  size_t ws_bytes, hipStream_t s);
 // coli_moe_route that also quantises x (Q8_0) into xq [T][H] / xd [T][H/32].
 int route_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, int32_t *topk_idx,
                 float *topk_w, void *workspace, size_t ws_bytes, int8_t *xq, float *xd, hipStream_t s);

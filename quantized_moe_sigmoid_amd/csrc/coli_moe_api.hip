@@ -166,6 +166,19 @@ int ffn_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x
                      workspace, L, s, nullptr, quantize_x, nullptr, shared, combine);
 }
 
+int combine_phase(const coli_moe_cfg *cfg, int32_t T, const float *topk_w, float *out, void *workspace,
+                  size_t ws_bytes, hipStream_t s) {
+  int st;
+  if ((st = check_cfg(cfg))) return st;
+  if ((st = check_T(cfg, T))) return st;
+  if (T == 0) return COLI_OK;
+  if (!topk_w || !out) return COLI_E_INVALID;
+  const WsLayout L = ws_layout(*cfg, T, route_ksplit(*cfg, T));
+  if (!workspace || ws_bytes < L.total) return COLI_E_WORKSPACE;
+  return dev(launch_combine(at<float>(workspace, L.ypair), topk_w, T, cfg->top_k, cfg->hidden, cfg->has_shared, out,
+                            s));
+}
+
 int route_phase(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, int32_t *topk_idx,
                 float *topk_w, void *workspace, size_t ws_bytes, int8_t *xq, float *xd, hipStream_t s) {
   int st;

@@ -11,33 +11,81 @@
 
 namespace {
 
-// Expert -> slot map of one tiered call, passed by value as a kernel argument (the
-// runtime copies arguments at launch, so the host map needs no lifetime beyond the
-// call and no synchronisation): slot of expert e, + TIER_MISS when e is copied in by
-// this call, -1 when e is not in the pool. E <= 1024 and slots <= E.
-constexpr int16_t TIER_MISS = 0x4000;
+// Expert -> slot map of one phase of a tiered call, passed by value as a kernel argument
+// (the runtime copies arguments at launch, so the host map needs no lifetime beyond the
+// call): slot of expert e, -1 when e is not served by the phase. E <= 1024, slots <= E.
 struct TierMap {
   int16_t slot[1024];
 };
 
-// The route in slot ids, split in two halves: s0 the pairs whose expert was resident,
-// s1 (when not null) the pairs whose expert is copied in by this call; the other half
-// holds -1, as does an empty slot (-1) of the route.
+// The route in slot ids of one phase: out[p] = slot of expert idx[p] in `map` (-1 when the
+// map has none, or for an empty slot of the route). host_idx (device-mapped pinned host
+// memory, when not null) receives the route itself.
 __global__ __launch_bounds__(256) void tier_remap_kernel(const int32_t *__restrict__ idx, int32_t P, TierMap map,
-                                                         int32_t *__restrict__ s0, int32_t *__restrict__ s1) {
+                                                         int32_t *__restrict__ out, int32_t *__restrict__ host_idx) {
   for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < P; p += gridDim.x * blockDim.x) {
     const int e = idx[p];
-    int a = -1, b = -1;
-    if (e >= 0 && e < 1024) {
-      const int v = map.slot[e];
-      if (v >= 0) {
-        if (v & TIER_MISS) b = v & (TIER_MISS - 1);
-        else a = v;
-      }
-    }
-    s0[p] = a;
-    if (s1) s1[p] = b;
+    out[p] = (e >= 0 && e < 1024) ? (int)map.slot[e] : -1;
+    if (host_idx) host_idx[p] = e;
   }
+}
+
+// The route's way to the host: pinned, device-mapped host memory that the remap kernel
+// writes, and an event recorded after it, per host thread (a tiered call waits for its
+// own event before it returns, so the thread's next call finds the buffer free). A
+// buffer that grows is replaced and the old one kept: nothing frees memory that a kernel
+// may have written.
+struct HostRoute {
+  int32_t *h = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev[64] = {};
+};
+thread_local HostRoute t_route;
+
+int32_t *host_route(size_t n) {
+  if (n > t_route.cap) {
+    size_t cap = t_route.cap ? 2 * t_route.cap : 4096;
+    while (cap < n) cap *= 2;
+    void *p = nullptr;
+    if (hipHostMalloc(&p, cap * sizeof(int32_t), hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent) !=
+        hipSuccess)
+      return nullptr;
+    t_route.h = static_cast<int32_t *>(p);
+    t_route.cap = cap;
+  }
+  return t_route.h;
+}
+
+hipEvent_t route_event(hipStream_t s) {
+  int dev = 0;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!t_route.ev[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (r != hipSuccess) return nullptr;
+    t_route.ev[dev] = e;
+  }
+  return t_route.ev[dev];
+}
+
+// The pool state is caller-owned memory: every slot and expert index must be in range
+// and the two maps must agree before any of it is used.
+bool tier_state_ok(const coli_tier &t) {
+  const int32_t E = t.n_experts, S = t.slots;
+  if (!t.slot_of || !t.expert_in || !t.last_use || E <= 0 || E > 1024 || S <= 0 || S > E) return false;
+  for (int32_t s = 0; s < S; s++) {
+    const int32_t e = t.expert_in[s];
+    if (e < -1 || e >= E || (e >= 0 && t.slot_of[e] != s)) return false;
+  }
+  for (int32_t e = 0; e < E; e++) {
+    const int32_t s = t.slot_of[e];
+    if (s < -1 || s >= S || (s >= 0 && t.expert_in[s] != e)) return false;
+  }
+  return true;
 }
 
 }  // namespace
@@ -71,14 +119,7 @@ int coli_tier_plan(coli_tier *t, const int32_t *topk_idx, int32_t T, int32_t k, 
     if (e >= 0) in_union[e] = 1;
   }
   // the state must be consistent (caller-owned memory): every index stays in range below
-  for (int32_t s = 0; s < S; s++) {
-    const int32_t e = t->expert_in[s];
-    if (e < -1 || e >= E || (e >= 0 && t->slot_of[e] != s)) return COLI_E_INVALID;
-  }
-  for (int32_t e = 0; e < E; e++) {
-    const int32_t s = t->slot_of[e];
-    if (s < -1 || s >= S || (s >= 0 && t->expert_in[s] != e)) return COLI_E_INVALID;
-  }
+  if (!tier_state_ok(*t)) return COLI_E_INVALID;
   std::vector<int32_t> misses;
   for (int32_t e = 0; e < E; e++)
     if (in_union[e] && t->slot_of[e] < 0) misses.push_back(e);
@@ -214,69 +255,82 @@ int coli_moe_layer_tiered(const coli_moe_cfg *cfg, const coli_moe_weights *w, co
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return COLI_E_ALIGN;
   if (!host_experts || !host_scales || !pool_experts || !pool_scales || !copy_stream || !copy_event)
     return COLI_E_INVALID;
+  if (!tier_state_ok(*tier)) return COLI_E_INVALID;
   const coli_moe_cfg pc = pool_cfg(*cfg, slots);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
   int32_t *idx = static_cast<int32_t *>(at(L.idx));
   float *wt = static_cast<float *>(at(L.w));
   hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+  hipEvent_t cev = static_cast<hipEvent_t>(copy_event);
   const size_t P = (size_t)T * k;
   const size_t a_bytes = L.ffn - L.route, b_bytes = L.idx - L.ffn;
-  int st;
-  // 1. route (quantising x into the FFN workspace), and the route on the host (the
-  // call's one host synchronisation)
-  if ((st = coli::route_phase(cfg, w, x, T, idx, wt, at(L.route), a_bytes, coli::ws_xq(pc, T, at(L.ffn)),
-                              coli::ws_xd(pc, T, at(L.ffn)), s)))
-    return st;
-  std::vector<int32_t> hidx(P), hs(P);
-  if (hipMemcpyAsync(hidx.data(), idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
-  if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;
-  // 2. plan
-  std::vector<int32_t> le(slots), ls(slots);
-  int32_t nl = 0;
-  if ((st = coli_tier_plan(tier, hidx.data(), T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
-  // the route in slot ids, split into the resident pairs and the missing pairs, on the
-  // device from the call's expert -> slot map
-  TierMap map;
-  for (int32_t e = 0; e < 1024; e++) map.slot[e] = (e < cfg->n_experts) ? (int16_t)tier->slot_of[e] : (int16_t)-1;
-  for (int32_t i = 0; i < nl; i++) map.slot[le[i]] = (int16_t)(ls[i] | TIER_MISS);
-  const int nphase = nl > 0 ? 2 : 1;
-  int32_t *sidx0 = static_cast<int32_t *>(at(L.sidx[0])), *sidx1 = static_cast<int32_t *>(at(L.sidx[1]));
-  hipLaunchKernelGGL(tier_remap_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, idx, (int32_t)P, map,
-                     sidx0, nphase == 2 ? sidx1 : nullptr);
-  if (hipGetLastError() != hipSuccess) return COLI_E_DEVICE;
-  // 3. copies already enqueued on the copy stream (a lookahead prefetch into this pool: the
-  // planner counts their experts as resident) are waited for before the first half; the
-  // wait takes the event as recorded here, before this call's own copies are enqueued
-  hipEvent_t ev = static_cast<hipEvent_t>(copy_event);
-  if (hipEventRecord(ev, cs) != hipSuccess) return COLI_E_DEVICE;
-  if (hipStreamWaitEvent(s, ev, 0) != hipSuccess) return COLI_E_DEVICE;
-  // the misses' copies, and the event the missing pairs wait for
-  if (nl > 0) {
-    if ((st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl, pool_experts,
-                                  pool_scales, copy_stream)))
-      return st;
-    if (hipEventRecord(static_cast<hipEvent_t>(copy_event), cs) != hipSuccess) return COLI_E_DEVICE;
-  }
-  const coli_moe_weights pw{pool_experts, static_cast<const float *>(pool_scales), w->router_w, w->router_bias};
-  for (int h = 0; h < nphase; h++) {
-    // 5. the missing pairs wait for their copies
-    if (h == 1 && hipStreamWaitEvent(s, static_cast<hipEvent_t>(copy_event), 0) != hipSuccess) return COLI_E_DEVICE;
+  const bool local = (int64_t)T * k <= coli::LOCAL_GROUP_MAX_P;
+  int32_t *hidx = host_route(P), *hidx_d = nullptr;
+  hipEvent_t rev = route_event(s);
+  if (!hidx || !rev || hipHostGetDevicePointer(reinterpret_cast<void **>(&hidx_d), hidx, 0) != hipSuccess)
+    return COLI_E_DEVICE;
+  const unsigned rgrid = (unsigned)((P + 255) / 256);
+  // one phase of the FFN on the pool: the pairs whose slot in sidx is set
+  auto phase = [&](int h, bool shared, bool combine) -> int {
     const int32_t *si = static_cast<const int32_t *>(at(L.sidx[h]));
     int32_t *cnt = static_cast<int32_t *>(at(L.cnt[h])), *off = static_cast<int32_t *>(at(L.off[h]));
     int32_t *perm = static_cast<int32_t *>(at(L.perm[h])), *act = static_cast<int32_t *>(at(L.act[h]));
     int32_t *nact = static_cast<int32_t *>(at(L.nact[h]));
+    int r;
     // batches past the decode size are grouped explicitly; smaller ones group inside the
     // GEMV workgroups
-    if ((int64_t)T * k > coli::LOCAL_GROUP_MAX_P &&
-        (st = coli_moe_group(&pc, si, T, cnt, off, perm, act, nact, stream)))
+    if (!local && (r = coli_moe_group(&pc, si, T, cnt, off, perm, act, nact, stream))) return r;
+    const coli_moe_weights pw{pool_experts, static_cast<const float *>(pool_scales), w->router_w, w->router_bias};
+    return coli::ffn_phase(&pc, &pw, x, T, si, wt, off, perm, act, nact, out, at(L.ffn), b_bytes, s, false, shared,
+                           combine);
+  };
+  int st;
+  // 1. route (quantising x into the FFN workspace)
+  if ((st = coli::route_phase(cfg, w, x, T, idx, wt, at(L.route), a_bytes, coli::ws_xq(pc, T, at(L.ffn)),
+                              coli::ws_xd(pc, T, at(L.ffn)), s)))
+    return st;
+  // 2. the route in slot ids of the experts the pool holds now (every pair of a miss is -1
+  // here), and the route itself into pinned host memory
+  TierMap map;
+  for (int32_t e = 0; e < 1024; e++) map.slot[e] = (e < cfg->n_experts) ? (int16_t)tier->slot_of[e] : (int16_t)-1;
+  hipLaunchKernelGGL(tier_remap_kernel, dim3(rgrid), dim3(256), 0, s, idx, (int32_t)P, map,
+                     static_cast<int32_t *>(at(L.sidx[0])), hidx_d);
+  if (hipGetLastError() != hipSuccess || hipEventRecord(rev, s) != hipSuccess) return COLI_E_DEVICE;
+  // 3. the resident pairs' FFN, the shared expert among them, is enqueued before the host
+  // plans. Copies already enqueued on the copy stream (a lookahead prefetch into this pool:
+  // its experts count as resident) are waited for first. Past this point the call waits
+  // for its route event before it returns, also on an error.
+  if (hipEventRecord(cev, cs) != hipSuccess || hipStreamWaitEvent(s, cev, 0) != hipSuccess) {
+    (void)hipEventSynchronize(rev);
+    return COLI_E_DEVICE;
+  }
+  if ((st = phase(0, true, false))) {
+    (void)hipEventSynchronize(rev);
+    return st;
+  }
+  // 4. the plan, on the host, from the route (the call's one wait for the device)
+  if (hipEventSynchronize(rev) != hipSuccess) return COLI_E_DEVICE;
+  std::vector<int32_t> hs(P), le(slots), ls(slots);
+  int32_t nl = 0;
+  if ((st = coli_tier_plan(tier, hidx, T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
+  if (nl > 0) {
+    // 5. the misses are copied on the copy stream; their pairs wait for the copies, then
+    // run with the combine over every slot of every token (the weights of the whole
+    // route, in slot order, over the pair rows both phases wrote)
+    if ((st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl, pool_experts,
+                                  pool_scales, copy_stream)))
       return st;
-    // 4./5. the FFN of this half. The first runs the shared expert (x was quantised by the
-    // route); the last sums every slot of every token (the weights of the whole route) in
-    // slot order over the pair rows both halves wrote into the shared FFN workspace.
-    if ((st = coli::ffn_phase(&pc, &pw, x, T, si, wt, off, perm, act, nact, out, at(L.ffn), b_bytes, s, false, h == 0,
-                              h == nphase - 1)))
-      return st;
+    if (hipEventRecord(cev, cs) != hipSuccess) return COLI_E_DEVICE;
+    TierMap miss;
+    for (int32_t e = 0; e < 1024; e++) miss.slot[e] = -1;
+    for (int32_t i = 0; i < nl; i++) miss.slot[le[i]] = (int16_t)ls[i];
+    hipLaunchKernelGGL(tier_remap_kernel, dim3(rgrid), dim3(256), 0, s, idx, (int32_t)P, miss,
+                       static_cast<int32_t *>(at(L.sidx[1])), static_cast<int32_t *>(nullptr));
+    if (hipGetLastError() != hipSuccess || hipStreamWaitEvent(s, cev, 0) != hipSuccess) return COLI_E_DEVICE;
+    if ((st = phase(1, false, true))) return st;
+  } else if ((st = coli::combine_phase(&pc, T, wt, out, at(L.ffn), b_bytes, s))) {
+    return st;
   }
   if (topk_idx_opt && hipMemcpyAsync(topk_idx_opt, idx, P * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return COLI_E_DEVICE;
@@ -305,12 +359,14 @@ int coli_moe_tier_prefetch(const coli_moe_cfg *cfg, const coli_moe_weights *w, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t P = (size_t)T * k;
   int st;
+  int32_t *hidx = host_route(P);
+  if (!hidx) return COLI_E_DEVICE;
   if ((st = coli_moe_route(cfg, w, x, T, idx, wt, ws + L.route, L.ffn - L.route, stream))) return st;
-  std::vector<int32_t> hidx(P), hs(P), le(slots), ls(slots);
-  if (hipMemcpyAsync(hidx.data(), idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
+  if (hipMemcpyAsync(hidx, idx, P * 4, hipMemcpyDeviceToHost, s) != hipSuccess) return COLI_E_DEVICE;
   if (hipStreamSynchronize(s) != hipSuccess) return COLI_E_DEVICE;
+  std::vector<int32_t> hs(P), le(slots), ls(slots);
   int32_t nl = 0;
-  if ((st = coli_tier_plan(tier, hidx.data(), T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
+  if ((st = coli_tier_plan(tier, hidx, T, k, hs.data(), le.data(), ls.data(), &nl))) return st;
   if (nl > 0 && (st = coli_moe_tier_stage(cfg, slots, host_experts, host_scales, le.data(), ls.data(), nl,
                                           pool_experts, pool_scales, copy_stream)))
     return st;
