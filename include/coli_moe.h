@@ -15,9 +15,11 @@
  * The pages leave the router's group rule, the bit layouts and the rounding
  * rules open; the readings this library implements are spelled out below.
  *
- * Conventions for every entry point:
+ * Conventions for every entry point (the expert tier's host-side calls, at the end of
+ * this header, state their own exceptions):
  *   - All array pointers are DEVICE pointers, allocated and owned by the caller.
- *     The library allocates no device memory and keeps no state between calls.
+ *     The library allocates no device memory and keeps no state between calls
+ *     (coli_moe_layer_noalloc runs on a scratch array the library holds, see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *     enqueued asynchronously; no call synchronises the stream or copies device
  *     data to the host.
@@ -224,7 +226,10 @@ const char *coli_moe_strerror(int status);
  * the pool unchanged, with cfg.n_experts = slots, the pool as coli_moe_weights.experts /
  * .scales, and the route remapped to slot ids: the expert arithmetic, the pair order and
  * the combine order are those of the resident layer, so the output is bit-identical to it.
- * The router lookahead (coli_moe_tier_prefetch) stages a layer's predicted union ahead. */
+ * The router lookahead (coli_moe_tier_prefetch) stages a layer's predicted union ahead.
+ * Unlike the entry points above, coli_moe_layer_tiered and coli_moe_tier_prefetch read the
+ * route on the host (each waits once for the device) and keep, per calling host thread, a
+ * pinned host buffer for it and, in coli_moe_layer_tiered, one event per device. */
 
 /* Host-side state of one layer's pool. All arrays are caller-owned host memory:
  * slot_of [n_experts], expert_in [slots], last_use [slots], pinned [n_experts]. */
