@@ -57,9 +57,29 @@ __device__ __forceinline__ uint32_t e2m1x4_to_i8x4(uint32_t n) {
   return (neg & msk) | (pos & ~msk);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 32 Q8_0 codes of a block (x[i] = codes 4 i .. 4 i + 3) -> 16 fp16 pairs (q_j, q_j+16):
+// a byte permute places q_j and q_j+16 over zero bytes, an XOR turns each half into
+// 0x64 : (q + 128), the fp16 number 1024 + q + 128, and one packed fp16 subtraction of
+// 1152 leaves q exactly.
+__device__ __forceinline__ void q8_to_f16_pairs(const int (&x)[8], uint32_t (&h)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
+      const uint32_t t = __builtin_amdgcn_perm((uint32_t)x[4 + i], (uint32_t)x[i], sel) ^ 0x64806480u;
+      h[4 * i + b] = as_u32(as_f16x2(t) - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
+    }
+}
+
 struct WsLayout {
   // byte offsets into the workspace (all 256-byte aligned)
-  size_t xq, xd, hq, hd, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, total;
+  size_t xq, xd, hq, hd, ypair, logits, idx, w, cnt, off, perm, active, nact, tiles, ntiles, redo, total;
 };
 
 // Workspace layout for T tokens (valid cfg assumed).
@@ -109,6 +129,7 @@ struct FfnArgs {
   float *hd;          // [P+T][F/32]
   float *ypair;       // [P+T][H]
   float *tap;         // test builds (COLI_TAPS) only: [P+T][2F] pre-SiLU g | u per output row
+  int32_t *redo;      // MXFP4 grouped GEMM: per work item, 1 = its scales need the integer path
 };
 
 // Test builds (compiled with COLI_TAPS) record the gate and up values of every output
@@ -137,6 +158,7 @@ hipError_t launch_gemv_w2(int mode, bool gs, const FfnArgs &a, hipStream_t s);
 hipError_t launch_gemv_mx(int mode, const FfnArgs &a, hipStream_t s);
 // grouped-GEMM (MFMA) path for batches whose experts see many tokens
 int32_t mfma_gmax(int32_t T, int32_t k, int32_t E, int32_t has_shared);  // token-tile capacity
+int64_t mfma_redo_words(const coli_moe_cfg &c, int32_t T);  // redo flags of an MXFP4 batch (0 otherwise)
 hipError_t launch_plan(const FfnArgs &a, int4 *tiles, int32_t *ntiles, int32_t gmax, hipStream_t s);
 hipError_t launch_mfma_gateup(int wfmt, const FfnArgs &a, const int4 *tiles, const int32_t *ntiles, int32_t gmax,
                               hipStream_t s);

@@ -34,6 +34,7 @@ WsLayout ws_layout(const coli_moe_cfg &c, int32_t T, int32_t ksplit) {
   L.nact = o;   o = align256(o + sizeof(int32_t));
   L.tiles = o;  o = align256(o + (size_t)mfma_gmax(T, c.top_k, c.n_experts, c.has_shared) * sizeof(int4));
   L.ntiles = o; o = align256(o + sizeof(int32_t));
+  L.redo = o;   o = align256(o + (size_t)mfma_redo_words(c, T) * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -131,6 +132,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   a.hd = at<float>(ws, L.hd);
   a.ypair = at<float>(ws, L.ypair);
   a.tap = tap;
+  a.redo = at<int32_t>(ws, L.redo);
   // Batches past the decode size run the expert FFNs as grouped GEMMs on the
   // matrix cores; a tile plan of the union comes first.
   const bool gemm = local_idx == nullptr && (int64_t)T * c.top_k > LOCAL_GROUP_MAX_P;

@@ -175,26 +175,6 @@ struct Unp {
 // exact in fp16, each product is exact in fp32 and every partial sum of a block is a
 // multiple of 1/2 below 2^15, so the fp32 sum is the block's exact J_b = sum e2m1 * q,
 // the same number as the integer path's 2 * J_b / 2.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
-__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
-
-// 32 Q8_0 codes of a block (x[i] = codes 4 i .. 4 i + 3) -> 16 fp16 pairs (q_j, q_j+16):
-// a byte permute places q_j and q_j+16 over zero bytes, an XOR turns each half into
-// 0x64 : (q + 128), the fp16 number 1024 + q + 128, and one packed fp16 subtraction of
-// 1152 leaves q exactly.
-__device__ __forceinline__ void q8_to_f16_pairs(const int (&x)[8], uint32_t (&h)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
-      const uint32_t t = __builtin_amdgcn_perm((uint32_t)x[4 + i], (uint32_t)x[i], sel) ^ 0x64806480u;
-      h[4 * i + b] = as_u32(as_f16x2(t) - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
-    }
-}
-
 template <int WB>
 __device__ __forceinline__ void unpack_chunk(const uint32_t (&wq)[Fmt<WB>::CHUNK / 4], int (&u)[Unp<WB>::N]) {
   if constexpr (WB == 4) {

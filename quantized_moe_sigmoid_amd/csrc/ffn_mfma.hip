@@ -29,6 +29,8 @@
 // takes one contiguous range of (row tile, chunk) work, chunks fastest: the chunks
 // of one heavy expert and row tile run on one XCD side by side and share its L2
 // copy of the weight rows.
+#include <type_traits>
+
 #include "coli_internal.h"
 
 namespace coli {
@@ -203,9 +205,11 @@ enum { MF_GATEUP = 0, MF_DOWN = 1 };
 // GS: one scale per group of G = GSZ<WB> inputs of a row (group scales; MXFP4's E8M0
 // per block): each block's scale is then d_b * s(row, group of b), applied per result;
 // otherwise one scale per row, applied in the epilogue.
+// One work item wk = (row tile, chunk) of the grouped GEMM; the kernels below map
+// workgroups to work items.
 template <int WB, int MODE, bool GS>
-__global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__restrict__ chunks,
-                                                   const int32_t *__restrict__ nchunks, int gmax, int nrt) {
+__device__ __forceinline__ void mfma_item(const FfnArgs &a, const int4 *__restrict__ chunks,
+                                          const int32_t *__restrict__ nchunks, int gmax, int wk) {
   constexpr int NMAT = (MODE == MF_GATEUP) ? 2 : 1;
   constexpr int G = GSZ<WB>;
   constexpr int NGS = GM_KB * QK / G;  // groups per stage: 2 (G = 64) or 4 (MXFP4)
@@ -213,11 +217,6 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   using Lds = GmLds<NMAT, NGS>;
   __shared__ Lds L;
 
-  // XCD-aware order: hardware workgroup i runs on XCD i % 8; give each XCD one
-  // contiguous range of work (chunks fastest)
-  const int nwork = nrt * gmax;  // a multiple of 8
-  const int bid = blockIdx.x;
-  const int wk = (bid & 7) * (nwork >> 3) + (bid >> 3);
   const int rt = wk / gmax, g = wk % gmax;
   if (g >= *nchunks) return;
   const int4 ch = chunks[g];  // expert, first perm index (-1: shared), tokens, first token
@@ -524,11 +523,335 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__r
   }
 }
 
+// XCD-aware order: hardware workgroup i runs on XCD i % 8; each XCD takes one contiguous
+// range of work items (chunks fastest), so the chunks of one heavy expert and row tile
+// run side by side on one XCD
+__device__ __forceinline__ int xcd_item(int bid, int nwork) { return (bid & 7) * (nwork >> 3) + (bid >> 3); }
+
+template <int WB, int MODE, bool GS>
+__global__ __launch_bounds__(256, 2) void mfma_kernel(FfnArgs a, const int4 *__restrict__ chunks,
+                                                   const int32_t *__restrict__ nchunks, int gmax, int nrt) {
+  mfma_item<WB, MODE, GS>(a, chunks, nchunks, gmax, xcd_item((int)blockIdx.x, nrt * gmax));
+}
+
+// The MXFP4 work items that mfma_mx_kernel flagged (a scale byte it cannot fold into the
+// fp16 convert), through the integer path. A small grid reads the flags 256 at a time and
+// computes the flagged items; with none flagged it costs one load per thread.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void mfma_redo_kernel(FfnArgs a, const int4 *__restrict__ chunks,
+                                                           const int32_t *__restrict__ nchunks, int gmax, int nrt) {
+  __shared__ int list[256];
+  __shared__ int cnt;
+  const int nwork = nrt * gmax, nch = *nchunks;
+  for (int base = (int)blockIdx.x * 256; base < nwork; base += (int)gridDim.x * 256) {
+    const int wk = base + (int)threadIdx.x;
+    const bool set = wk < nwork && wk % gmax < nch && a.redo[wk] != 0;
+    if (threadIdx.x == 0) cnt = 0;
+    __syncthreads();
+    if (set) list[atomicAdd(&cnt, 1)] = wk;
+    __syncthreads();
+    const int n = cnt;
+    for (int i = 0; i < n; i++) {
+      mfma_item<W_MX, MODE, true>(a, chunks, nchunks, gmax, list[i]);
+      __syncthreads();  // the next item reuses the item's LDS
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MXFP4 on the fp16 matrix cores
+// MXFP4 weights take the fp16 MFMA (v_mfma_f32_32x32x16_f16, two per Q8_0 block) instead
+// of widening the codes to int8:
+//   - the hardware fp4 -> fp16 convert (v_cvt_scalef32_pk_f16_fp4) multiplies by the
+//     block's E8M0 scale s = 2^(u - 127) on the way; e2m1 * s is exact and a normal fp16
+//     number for every code when 114 <= u <= 140 (0.5 s >= 2^-14, 6 s <= 65504);
+//   - the tokens' Q8_0 codes are staged in LDS as fp16 (exact, |q| <= 127);
+//   - each product (e2m1 s) q is exact in fp32, and every partial sum of a block is a
+//     multiple of s / 2 with fewer than 2^24 such units, so the MFMAs return s J_b exactly
+//     (J_b = sum e2m1 q, the block dot of the definition);
+//   - the scaling is one multiply-add per result, acc += d_b (s J_b): the single rounding
+//     of d_b s J_b + acc, the same number the integer path forms as (d_b s) * J_b.
+// A workgroup that meets a scale byte outside that range writes nothing and flags its work
+// item; a second launch of the integer kernel (mfma_kernel<W_MX, MODE, true>) computes the
+// flagged items only, with the same sums. Keeping that path out of this kernel keeps its
+// registers and code small (2030 against 2374 us at the GLM-scale prefill with it inline).
+// K order: the convert of byte j of a block gives the pair (K_j, K_j+16), and both
+// operands take their fp16 pairs in that order (A: the pair of byte j; B: (q_j, q_j+16)).
+// Lane half hl covers bytes 8 hl .. 8 hl + 7 of each block, the first MFMA bytes
+// 8 hl + 0..3 and the second 8 hl + 4..7; an MFMA multiplies A and B slot by slot, so
+// any K order shared by both operands gives the same sums.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int MX_XROW = GM_KB * 16 + 4;  // LDS dwords per token row of a stage: 4 blocks x 16 pairs + padding
+constexpr uint32_t MX_FOLD_LO = 114, MX_FOLD_HI = 140;
+
+struct MxLds {
+  // fp16 pairs (q_j, q_j+16) of the stage's blocks; 16-byte aligned so that a lane's
+  // eight fp16 of a B operand are one ds_read_b128
+  __attribute__((aligned(16))) uint32_t x[2][GM_TOK][MX_XROW];
+  float d[2][GM_TOK][GM_KB];       // their block scales
+  int bad[4];                      // per wavefront: a scale byte outside the folding range
+  int act[GM_TOK];
+  int outr[GM_TOK];
+};
+
+__device__ __forceinline__ bool mx_foldable(uint32_t w) {  // every scale byte of w in range
+  bool ok = true;
+#pragma unroll
+  for (int b = 0; b < 4; b++) ok = ok && (((w >> (8 * b)) & 0xFFu) - MX_FOLD_LO) <= (MX_FOLD_HI - MX_FOLD_LO);
+  return ok;
+}
+
+// A operands of one block: eight fp16 pairs from two dwords of codes, times `s`.
+__device__ __forceinline__ void mx_a(uint32_t w_lo, uint32_t w_hi, float s, v8h &a_lo, v8h &a_hi) {
+  a_lo = __builtin_bit_cast(v8h, make_uint4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_lo, s, 0)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_lo, s, 1)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_lo, s, 2)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_lo, s, 3))));
+  a_hi = __builtin_bit_cast(v8h, make_uint4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_hi, s, 0)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_hi, s, 1)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_hi, s, 2)),
+                                             as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w_hi, s, 3))));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void mfma_mx_kernel(FfnArgs a, const int4 *__restrict__ chunks,
+                                                         const int32_t *__restrict__ nchunks, int gmax, int nrt) {
+  constexpr int NMAT = (MODE == MF_GATEUP) ? 2 : 1;
+  constexpr int NL = Top<W_MX>::loads;  // two 16-byte pieces per matrix and stage
+  __shared__ MxLds L;
+
+  // work item, chunk and token slots: as mfma_item
+  const int wk = xcd_item((int)blockIdx.x, nrt * gmax);
+  const int rt = wk / gmax, g = wk % gmax;
+  if (g >= *nchunks) return;
+  const int4 ch = chunks[g];
+  const int n = ch.z;
+  const int nt = __builtin_amdgcn_readfirstlane((n + 31) >> 5);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int K = (MODE == MF_GATEUP) ? a.H : a.F;
+  const int nkb = K / QK;
+  const int ns = nkb / GM_KB;
+  const int P = a.T * a.k;
+  const int64_t rb = row_bytes(W_MX, K);
+  const int64_t rbh = row_bytes(W_MX, a.H);
+  const int r0 = rt * GM_ROWS;
+  const uint8_t *blob = a.experts + (int64_t)ch.x * a.blob_bytes;
+  const uint8_t *mat0 = (MODE == MF_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
+  const uint8_t *mat1 = blob + (int64_t)a.F * rbh;
+  const int row = r0 + 32 * wv + li;  // this lane's weight row
+  const int64_t arow = (int64_t)row * rb;
+  // E8M0 bytes of the lane's row (gate [F][H/32] | up [F][H/32] | down [H][F/32]): the
+  // four of a stage are one dword
+  const uint8_t *sbase = reinterpret_cast<const uint8_t *>(a.scales) + (int64_t)ch.x * a.scale_stride;
+  const int64_t ngh = (int64_t)a.F * (a.H / QK);
+  const uint8_t *srow0 = sbase + ((MODE == MF_GATEUP) ? 0 : 2 * ngh) + (int64_t)row * nkb;
+  const uint8_t *srow1 = sbase + ngh + (int64_t)row * nkb;
+
+  if (tid < GM_TOK) {
+    const int i = ch.w + (tid < n ? tid : 0);
+    int act, outr;
+    if (ch.y < 0) {
+      outr = P + i;
+      act = (MODE == MF_GATEUP) ? i : P + i;
+    } else {
+      const int p = a.perm[ch.y + i];
+      outr = p;
+      act = (MODE == MF_GATEUP) ? p / a.k : p;
+    }
+    L.act[tid] = act;
+    L.outr[tid] = tid < n ? outr : -1;
+  }
+  __syncthreads();
+
+  const int8_t *asrc = (MODE == MF_GATEUP) ? a.xq : a.hq;
+  const float *dsrc = (MODE == MF_GATEUP) ? a.xd : a.hd;
+  // activation staging: thread tid takes block tid % 4 of the stage for token slot tid / 4
+  const int st_tok = tid >> 2, st_kb = tid & 3;
+  const bool st_on = st_tok < 32 * nt;
+  const int64_t xoff = (int64_t)L.act[st_tok] * K + st_kb * QK;
+  const int64_t doff = (int64_t)L.act[st_tok] * nkb + st_kb;
+
+  uint4 w0[NMAT][NL], w1[NMAT][NL];
+  uint32_t u0[NMAT], u1[NMAT];  // the stage's scale bytes of the lane's row
+  auto wload = [&](int s, uint4 (&wr)[NMAT][NL], uint32_t (&ur)[NMAT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NMAT; m++) {
+#pragma unroll
+      for (int j = 0; j < NL; j++)
+        wr[m][j] = *reinterpret_cast<const uint4 *>((m == 0 ? mat0 : mat1) + arow + a_piece<W_MX>(s, j, h));
+      ur[m] = *reinterpret_cast<const uint32_t *>((m == 0 ? srow0 : srow1) + s * GM_KB);
+    }
+  };
+  uint4 xr0 = make_uint4(0, 0, 0, 0), xr1 = make_uint4(0, 0, 0, 0);
+  float dr = 0.0f;
+  auto gload = [&](int s) __attribute__((always_inline)) {
+    if (st_on) {
+      const int8_t *p = asrc + xoff + (int64_t)s * (GM_KB * QK);
+      xr0 = *reinterpret_cast<const uint4 *>(p);
+      xr1 = *reinterpret_cast<const uint4 *>(p + 16);
+      dr = dsrc[doff + s * GM_KB];
+    }
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+    if (st_on) {
+      const int x[8] = {(int)xr0.x, (int)xr0.y, (int)xr0.z, (int)xr0.w, (int)xr1.x, (int)xr1.y, (int)xr1.z, (int)xr1.w};
+      uint32_t hp[16];
+      q8_to_f16_pairs(x, hp);
+      uint4 *dst = reinterpret_cast<uint4 *>(&L.x[buf][st_tok][16 * st_kb]);
+#pragma unroll
+      for (int q = 0; q < 4; q++) dst[q] = make_uint4(hp[4 * q], hp[4 * q + 1], hp[4 * q + 2], hp[4 * q + 3]);
+      L.d[buf][st_tok][st_kb] = dr;
+    }
+  };
+
+  float acc[NMAT][GM_TILES][16];
+#pragma unroll
+  for (int m = 0; m < NMAT; m++)
+#pragma unroll
+    for (int t = 0; t < GM_TILES; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[m][t][r] = 0.0f;
+
+  // one stage: s rides in the convert (lanes whose row has a byte out of range compute
+  // garbage and mark the work item for the integer path)
+  bool bad = false;
+  auto compute = [&](int buf, const uint4 (&wc)[NMAT][NL], const uint32_t (&uc)[NMAT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NMAT; m++) bad = bad || !mx_foldable(uc[m]);
+#pragma unroll
+    for (int jp = 0; jp < 2; jp++) {
+      // lanes 0-31 hold block 4s + 2 jp, lanes 32-63 block 4s + 2 jp + 1; after the swaps
+      // each lane holds bytes 8 h .. 8 h + 7 of both: wd[m][i][0..1] for block 2 jp + i
+      uint32_t wd[NMAT][2][2];
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) {
+        uint32_t x0 = wc[m][jp].x, z0 = wc[m][jp].z, y0 = wc[m][jp].y, w0_ = wc[m][jp].w;
+        swap32(x0, z0);
+        swap32(y0, w0_);
+        wd[m][0][0] = x0;
+        wd[m][0][1] = y0;
+        wd[m][1][0] = z0;
+        wd[m][1][1] = w0_;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int kb = 2 * jp + i;
+        v8h alo[NMAT], ahi[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+          mx_a(wd[m][i][0], wd[m][i][1], __uint_as_float(((uc[m] >> (8 * kb)) & 0xFFu) << 23), alo[m], ahi[m]);
+#pragma unroll
+        for (int t = 0; t < GM_TILES; t++) {
+          if (t >= nt) continue;
+          const v8h blo = *reinterpret_cast<const v8h *>(&L.x[buf][32 * t + li][16 * kb + 8 * h]);
+          const v8h bhi = *reinterpret_cast<const v8h *>(&L.x[buf][32 * t + li][16 * kb + 8 * h + 4]);
+          const float d = L.d[buf][32 * t + li][kb];
+#pragma unroll
+          for (int m = 0; m < NMAT; m++) {
+            const v16f zero = {};
+            v16f D = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[m], blo, zero, 0, 0, 0);
+            D = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[m], bhi, D, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[m][t][r] = fmaf(d, D[r], acc[m][t][r]);
+          }
+        }
+      }
+    }
+  };
+
+  auto lds_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0 (gfx9 encoding)
+    __builtin_amdgcn_s_barrier();
+  };
+  gload(0);
+  lstore(0);
+  wload(0, w0, u0);
+  lds_barrier();
+  auto body = [&](int s, const uint4 (&wc)[NMAT][NL], const uint32_t (&uc)[NMAT], uint4 (&wn)[NMAT][NL],
+                  uint32_t (&un)[NMAT]) __attribute__((always_inline)) {
+    if (s + 1 < ns) gload(s + 1);
+    if (s + 1 < ns) wload(s + 1, wn, un);
+    compute(s & 1, wc, uc);
+    if (s + 1 < ns) lstore((s + 1) & 1);
+    lds_barrier();
+  };
+  for (int s = 0; s < ns; s += 2) {
+    body(s, w0, u0, w1, u1);
+    if (s + 1 < ns) body(s + 1, w1, u1, w0, u0);
+  }
+
+  // a work item with any scale byte out of range is left to the integer kernel
+  if (lane == 0) L.bad[wv] = __any(bad) ? 1 : 0;
+  __syncthreads();
+  const int redo = L.bad[0] | L.bad[1] | L.bad[2] | L.bad[3];
+  if (tid == 0) a.redo[wk] = redo;
+  if (redo) return;
+
+  // epilogue: result r of this lane in tile t is row r0 + 32 wv + 8 (r / 4) + 4 h + r % 4,
+  // token slot 32 t + li; the sums carry every scale (no row scales with MXFP4)
+  const int rw = 32 * wv + 4 * h;
+#pragma unroll
+  for (int t = 0; t < GM_TILES; t++) {
+    if (t >= nt) continue;
+    const int out_row = L.outr[32 * t + li];
+    const bool valid = out_row >= 0;
+    if constexpr (MODE == MF_GATEUP) {
+      float hv[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int rl = rw + 8 * (r >> 2) + (r & 3);
+        const float gv = acc[0][t][r], uv = acc[1][t][r];
+        if (valid) COLI_TAP_GU(a, out_row, r0 + rl, gv, uv);
+        hv[r] = (gv / (1.0f + expf(-gv))) * uv;
+        amax = fmaxf(amax, fabsf(hv[r]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float d = amax / 127.0f;
+      uint32_t packed[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          int c = 0;
+          if (d != 0.0f) c = (int)fminf(fmaxf(roundf(hv[4 * q + j] / d), -127.0f), 127.0f);
+          pk |= (uint32_t)(c & 0xFF) << (8 * j);
+        }
+        packed[q] = pk;
+      }
+      if (valid) {
+        int8_t *hrow = a.hq + (int64_t)out_row * a.F + r0 + rw;
+#pragma unroll
+        for (int q = 0; q < 4; q++) *reinterpret_cast<uint32_t *>(hrow + 8 * q) = packed[q];
+        if (h == 0) a.hd[(int64_t)out_row * (a.F / QK) + (r0 + 32 * wv) / QK] = d;
+      }
+    } else {
+      if (valid) {
+        float *yrow = a.ypair + (int64_t)out_row * a.H + r0 + rw;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          *reinterpret_cast<float4 *>(yrow + 8 * q) =
+              make_float4(acc[0][t][4 * q], acc[0][t][4 * q + 1], acc[0][t][4 * q + 2], acc[0][t][4 * q + 3]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 int32_t mfma_gmax(int32_t T, int32_t k, int32_t E, int32_t has_shared) {
   const int64_t rows = (int64_t)T * k + (int64_t)has_shared * T;
   const int64_t g = (rows + GM_TOK - 1) / GM_TOK + E + has_shared;
   return (int32_t)((g + 7) / 8 * 8);
+}
+
+int64_t mfma_redo_words(const coli_moe_cfg &c, int32_t T) {
+  if (c.wfmt != W_MX || (int64_t)T * c.top_k <= LOCAL_GROUP_MAX_P) return 0;
+  return (int64_t)mfma_gmax(T, c.top_k, c.n_experts, c.has_shared) * (max(c.hidden, c.ffn) / GM_ROWS);
 }
 
 hipError_t launch_plan(const FfnArgs &a, int4 *chunks, int32_t *nchunks, int32_t gmax, hipStream_t s) {
@@ -548,10 +871,16 @@ static hipError_t launch_mf(const FfnArgs &a, const int4 *chunks, const int32_t 
   const int nrt = rows / GM_ROWS;
   const int64_t nwork = (int64_t)nrt * gmax;
   if (nwork > 0x7fffffff) return hipErrorInvalidValue;
-  if (WB == W_MX || a.gs)  // MXFP4 always takes the group-scale path (a.gs == 32 checked above)
+  if constexpr (WB == W_MX) {
+    // the fp16 kernel, then the integer kernel for the work items it flagged
+    hipLaunchKernelGGL((mfma_mx_kernel<MODE>), dim3((unsigned)nwork), dim3(256), 0, s, a, chunks, nchunks, gmax, nrt);
+    const int64_t rg = (nwork + 255) / 256;
+    hipLaunchKernelGGL((mfma_redo_kernel<MODE>), dim3((unsigned)(rg < 256 ? rg : 256)), dim3(256), 0, s, a, chunks,
+                       nchunks, gmax, nrt);
+  } else if (a.gs)
     hipLaunchKernelGGL((mfma_kernel<WB, MODE, true>), dim3((unsigned)nwork), dim3(256), 0, s, a, chunks, nchunks,
                        gmax, nrt);
-  else if constexpr (WB != W_MX)
+  else
     hipLaunchKernelGGL((mfma_kernel<WB, MODE, false>), dim3((unsigned)nwork), dim3(256), 0, s, a, chunks, nchunks,
                        gmax, nrt);
   return hipGetLastError();

@@ -121,6 +121,38 @@ def test_mxfp4_exact_case_bitidentical(q, orc, T):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("T", [11, 530])
+def test_mxfp4_exact_case_row_scales_bitidentical(q, orc, T):
+    """The exact case with one E8M0 byte per row, varied over rows: gate 142 (2^15), up
+    113 (2^-14) and down 147 (2^20) on some rows, 127 elsewhere. Every product and sum stays
+    exact, so the output is bit-identical to the oracle's. The grouped GEMM (T = 530) folds
+    a scale into the fp16 convert only for bytes 114..140 (e2m1 * s a normal fp16 number):
+    wavefronts holding a 142, 113 or 147 row take the per-result path, the others the
+    folded one, in the same launch."""
+    print(f"mxfp4 exact row scales T={T}", flush=True)
+    H, F, E = 256, 128, 6
+    x, blobs, scales = _exact_mx_inputs(H, F, E, T, 310 + T)
+    nb_h, nb_f = H // 32, F // 32
+    gate = np.full((E, F, nb_h), 127, np.uint8)
+    up = np.full((E, F, nb_h), 127, np.uint8)
+    down = np.full((E, H, nb_f), 127, np.uint8)
+    rows_f, rows_h = np.arange(F), np.arange(H)
+    gate[:, ((rows_f // 32) % 2 == 1) & (rows_f % 3 == 0), :] = 142   # every other wavefront's rows
+    up[:, ((rows_f // 32) % 2 == 1) & (rows_f % 5 == 1), :] = 113
+    down[:, ((rows_h // 32) % 2 == 0) & (rows_h % 4 == 0), :] = 147
+    scales = np.concatenate([gate.reshape(E, -1), up.reshape(E, -1), down.reshape(E, -1)], axis=1)
+    assert scales.shape[1] == 3 * F * H // 32
+    cfgd = _cfg(hidden=H, ffn=F, n_experts=E, top_k=1, rsf=1.0)
+    rw = synth.router_weight(3, 0, E, H, std=0.001)
+    rb = synth.router_bias(3, 0, E)
+    inp = dict(x=x, blobs=blobs, scales=scales, router_w=rw, router_bias=rb)
+    out, idx, _ = gu.run_layer(cfgd, gu.upload_layer(inp), x)
+    ref, ridx, _ = orc.layer(orc.make_cfg(**cfgd), blobs, scales, rw, rb, x)
+    assert np.array_equal(idx, ridx)
+    assert np.abs(ref).max() > 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
 def test_mxfp4_scales_reach_the_kernels(q, orc):
     """Doubling one block's scale (E8M0 byte + 1) in every row changes the GPU output
     exactly as it changes the oracle's."""
