@@ -198,7 +198,7 @@ int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const flo
  * zero, and the contents left by the previous call are never read.
  * Returns COLI_E_SCRATCH, with nothing enqueued, when the batch needs more scratch than
  * that (coli_moe_workspace_bytes(cfg, T) > coli_moe_scratch_bytes(): GLM-5.2-scale decode
- * fits up to T = 64, OLMoE-scale up to T = 128); otherwise arguments, results and
+ * fits up to T = 112, OLMoE-scale up to T = 412); otherwise arguments, results and
  * statuses are those of coli_moe_layer, bit for bit. */
 size_t coli_moe_scratch_bytes(void);
 int coli_moe_layer_noalloc(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
