@@ -209,3 +209,52 @@ def test_router_lookahead_prefetch_then_layer_bitidentical(q):
     ev.close()
     assert prefetched > 0
     print(f"prefetched {prefetched} experts, {later_loads} loaded on demand", flush=True)
+
+
+def test_layer_tiered_union_too_large_leaves_out_and_tier_untouched(q):
+    """A union larger than the pool: the call returns COLI_E_UNSUPPORTED after its route and
+    the resident experts' phase; `out` keeps its contents, the tier state (maps, clocks) is
+    unchanged, and the next call that fits still equals the resident layer bit for bit."""
+    import torch
+    import quantized_moe_sigmoid_amd as qq
+    d = gu.dev()
+    E, slots, T = 32, 4, 6
+    cfgd = dict(hidden=512, ffn=256, n_experts=E, top_k=4, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
+                wbits=4, scale_group=0)
+    inp = synth.layer_inputs(830, 0, tokens=1, hidden=512, ffn=256, n_experts=E, has_shared=True, wbits=4)
+    cfg = q.make_cfg(**cfgd)
+    blob, nsc = q.blob_bytes(cfg), q.scales_per_expert(cfg)
+    resident = gu.upload_layer(inp)
+    hb = torch.from_numpy(np.ascontiguousarray(inp["blobs"]).reshape(-1)).pin_memory()
+    hs = torch.from_numpy(np.ascontiguousarray(inp["scales"]).reshape(-1)).pin_memory()
+    pool_b = torch.zeros((slots + 1) * blob, dtype=torch.uint8, device=d)
+    pool_s = torch.zeros((slots + 1) * nsc, dtype=torch.float32, device=d)
+    tier = q.Tier(E, slots)
+    q.tier_stage(cfg, slots, hb, hs, [E], [slots], pool_b, pool_s)
+    cs = torch.cuda.Stream(d)
+    ev = q.HipEvent()
+    ws = q.alloc_tier_workspace(cfg, slots, T, d)
+    # one token first: its union (4 experts) fills the pool
+    x1_np = synth.activations(830, 0, 1, 512, index=0)
+    out1 = torch.empty((1, 512), dtype=torch.float32, device=d)
+    q.layer_tiered(cfg, resident, tier, hb, hs, pool_b, pool_s, gu.to_dev(x1_np), out1, ws, cs, ev)
+    torch.cuda.synchronize()
+    before = (tier.slot_of.copy(), tier.expert_in.copy(), tier.last_use.copy(), int(tier.c.clock))
+    x_np = synth.activations(830, 0, T, 512, index=1)
+    out = torch.full((T, 512), float("nan"), dtype=torch.float32, device=d)
+    print(f"tiered union too large T={T} slots={slots}", flush=True)
+    with pytest.raises(qq.ColiError) as ei:
+        q.layer_tiered(cfg, resident, tier, hb, hs, pool_b, pool_s, gu.to_dev(x_np), out, ws, cs, ev)
+    assert ei.value.status == qq.COLI_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    assert np.array_equal(tier.slot_of, before[0]) and np.array_equal(tier.expert_in, before[1])
+    assert np.array_equal(tier.last_use, before[2]) and int(tier.c.clock) == before[3]
+    # a batch that fits afterwards
+    out2 = torch.empty((1, 512), dtype=torch.float32, device=d)
+    x2_np = synth.activations(830, 0, 1, 512, index=2)
+    q.layer_tiered(cfg, resident, tier, hb, hs, pool_b, pool_s, gu.to_dev(x2_np), out2, ws, cs, ev)
+    ref, _, _ = gu.run_layer(cfgd, resident, x2_np)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    ev.close()
