@@ -1413,7 +1413,11 @@ static int resident_groups(Kern k, int threads) {
 template <int WB, int LPR, int MODE, bool GS>
 static hipError_t launch_pipe(const FfnArgs &a, int nrows, hipStream_t s) {
   constexpr int WRMAX = 64 * (WAVE / LPR) / (Fmt<WB>::CHUNK / 4);
-  constexpr int WR = (MODE == MODE_DOWN) ? (WRMAX < 16 ? WRMAX : 16) : 8;
+  // rows per wavefront: 8, or 16 for down rows of at most 32 lanes (a row of 64 lanes is
+  // 16 KB of loads per wavefront at 16 rows; 8 measured faster there: GLM-scale down at
+  // T = 16 104.8 -> 102.9 us, T = 1 14.9 -> 13.3 us, while OLMoE-scale down, 32 lanes
+  // per row, lost 1.7 us at 8)
+  constexpr int WR = (MODE == MODE_DOWN && LPR < 64) ? (WRMAX < 16 ? WRMAX : 16) : 8;
   constexpr int TILE = 4 * WR;
   if (nrows % TILE) return hipErrorNotSupported;
   auto kern = gemv_pipe_kernel<WB, LPR, MODE, WR, GS>;
