@@ -571,9 +571,10 @@ __global__ __launch_bounds__(256, 2) void mfma_redo_kernel(FfnArgs a, const int4
 //   - the scaling is one multiply-add per result, acc += d_b (s J_b): the single rounding
 //     of d_b s J_b + acc, the same number the integer path forms as (d_b s) * J_b.
 // A workgroup that meets a scale byte outside that range writes nothing and flags its work
-// item; a second launch of the integer kernel (mfma_kernel<W_MX, MODE, true>) computes the
-// flagged items only, with the same sums. Keeping that path out of this kernel keeps its
-// registers and code small (2030 against 2374 us at the GLM-scale prefill with it inline).
+// item; a second launch (mfma_redo_kernel) runs the flagged items only through the integer
+// path (mfma_item<W_MX, MODE, true>), with the same sums. Keeping that path out of this
+// kernel keeps its registers and code small (gate/up 2030 against 2374 us at the GLM-scale
+// prefill with it inline).
 // K order: the convert of byte j of a block gives the pair (K_j, K_j+16), and both
 // operands take their fp16 pairs in that order (A: the pair of byte j; B: (q_j, q_j+16)).
 // Lane half hl covers bytes 8 hl .. 8 hl + 7 of each block, the first MFMA bytes
