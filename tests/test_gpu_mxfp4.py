@@ -153,6 +153,24 @@ def test_mxfp4_exact_case_row_scales_bitidentical(q, orc, T):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("H,F,T", [(512, 2048, 11), (6144, 256, 5)])
+def test_mxfp4_exact_case_long_rows_bitidentical(q, orc, H, F, T):
+    """The exact case at GLM-scale row lengths (down rows of 2048 inputs, gate/up rows of
+    6144), MXFP4, decode sizes."""
+    print(f"mxfp4 exact long rows H={H} F={F} T={T}", flush=True)
+    E = 6
+    x, blobs, scales = _exact_mx_inputs(H, F, E, T, 320 + H // 256 + F // 256)
+    cfgd = _cfg(hidden=H, ffn=F, n_experts=E, top_k=1, rsf=1.0)
+    rw = synth.router_weight(3, 0, E, H, std=0.001)
+    rb = synth.router_bias(3, 0, E)
+    inp = dict(x=x, blobs=blobs, scales=scales, router_w=rw, router_bias=rb)
+    out, idx, _ = gu.run_layer(cfgd, gu.upload_layer(inp), x)
+    ref, ridx, _ = orc.layer(orc.make_cfg(**cfgd), blobs, scales, rw, rb, x)
+    assert np.array_equal(idx, ridx)
+    assert np.abs(ref).max() > 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
 def test_mxfp4_scales_reach_the_kernels(q, orc):
     """Doubling one block's scale (E8M0 byte + 1) in every row changes the GPU output
     exactly as it changes the oracle's."""

@@ -348,6 +348,26 @@ def test_layer_exact_case_bitidentical(q, orc, wbits, T):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("H,F,T", [(512, 2048, 11), (6144, 256, 5), (6144, 2048, 3)])
+def test_layer_exact_case_long_rows_bitidentical(q, orc, H, F, T):
+    """The exact case at the row lengths of the GLM-scale kernels: down rows of 2048 inputs
+    (one 16-byte chunk per lane over 64 lanes: the pipelined down GEMV, 8 rows per
+    wavefront) and gate/up rows of 6144 inputs (three chunks per lane: the software-
+    pipelined batched GEMV), int4, decode sizes."""
+    print(f"exact long rows H={H} F={F} T={T}", flush=True)
+    E = 6
+    x, blobs, scales = _exact_inputs(H, F, E, 4, T, 400 + H // 256 + F // 256)
+    cfgd = _cfg(hidden=H, ffn=F, n_experts=E, top_k=1, rsf=1.0, wbits=4)
+    rw = synth.router_weight(5, 0, E, H, std=0.001)
+    rb = synth.router_bias(5, 0, E)
+    inp = dict(x=x, blobs=blobs, scales=scales, router_w=rw, router_bias=rb)
+    out, idx, _ = gu.run_layer(cfgd, gu.upload_layer(inp), x)
+    ref, ridx, _ = orc.layer(orc.make_cfg(**cfgd), blobs, scales, rw, rb, x)
+    assert np.array_equal(idx, ridx)
+    assert np.abs(ref).max() > 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("wbits,T", [(4, 13), (8, 13), (2, 13), (4, 181), (8, 181), (2, 181)])
 def test_shared_expert_exact_case_bitidentical(q, orc, wbits, T):
     """Routed experts with all-zero down rows contribute exact zeros, so the output is
