@@ -1,5 +1,6 @@
 // ffn_mfma.hip — expert FFNs of large batches (prefill, long verify) as grouped
-// GEMMs on the int8 matrix cores of gfx950 (v_mfma_i32_32x32x32_i8).
+// GEMMs on the int8 matrix cores of gfx950 (v_mfma_i32_32x32x32_i8); MXFP4 weights on
+// the fp16 matrix cores instead (mfma_mx_kernel, further down).
 //
 // Batch-union (colibri-strix README, "What's implemented", batch-union item): each
 // expert of the union is one GEMM of its weight rows against the Q8_0 rows of the
@@ -28,7 +29,8 @@
 // Token chunks are listed by plan_kernel; the 1-D grid is remapped so that each XCD
 // takes one contiguous range of (row tile, chunk) work, chunks fastest: the chunks
 // of one heavy expert and row tile run on one XCD side by side and share its L2
-// copy of the weight rows.
+// copy of the weight rows. mfma_item is the work of one (row tile, chunk) item;
+// mfma_kernel runs one item per workgroup.
 #include <type_traits>
 
 #include "coli_internal.h"
