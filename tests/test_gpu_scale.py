@@ -104,10 +104,12 @@ def test_glm_verify_lowbit_full(env, wbits):
 
 @pytest.mark.parametrize("fmt", ["gs64", "mxfp4"])
 def test_decode_full_other_scale_formats(env, fmt):
-    """Group-scaled int4 and MXFP4 weights at the OLMoE and GLM decode sizes."""
+    """Group-scaled int4 and MXFP4 weights at the OLMoE and GLM decode sizes, every token
+    (GLM T = 1, 4 and 16 take different GEMV paths)."""
     kw = dict(scale_group=64) if fmt == "gs64" else dict(wbits=synth.W_MXFP4)
     _run(env, 1, 16, range(16), **kw)
-    _run(env, 2, 16, [0, 8, 15], **kw)
+    for T in (1, 4, 16):
+        _run(env, 2, T, range(T), **kw)
 
 
 @pytest.mark.parametrize("fmt", ["gs64", "mxfp4"])
