@@ -731,11 +731,10 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   const int ks = r.ksplit;
   bool x_done = false;  // x quantised by the logits kernel
   if (T <= LD_TT && H % 256 == 0) {
+    // route_ksplit gives 256-wide K chunks here (one float4 per lane and row)
+    if (H / ks != 256) return hipErrorInvalidValue;
     dim3 grid((E + 4 * LD_EPW - 1) / (4 * LD_EPW), ks);
-    if (H / ks == 512)
-      hipLaunchKernelGGL(logits_decode_kernel<2>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
-    else
-      hipLaunchKernelGGL(logits_decode_kernel<1>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
+    hipLaunchKernelGGL(logits_decode_kernel<1>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
     x_done = true;
   } else if (T <= LD_TT) {
     dim3 grid((E + 15) / 16, 1, ks);
