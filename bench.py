@@ -31,7 +31,8 @@ INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, AMD public specification
 DOMINANT_STAGE = "ffn_gate_up"
 METRIC = "MoE-layer tokens/s + int4 weight GB/s vs HBM peak (decode); int8 TOPS (prefill)"
 KERNEL_SOURCES = ["quantized_moe_sigmoid_amd/csrc/coli_internal.h", "quantized_moe_sigmoid_amd/csrc/ffn_gemv_impl.h",
-                  "quantized_moe_sigmoid_amd/csrc/ffn_gemv_w4.hip", "quantized_moe_sigmoid_amd/csrc/ffn_mfma.hip"]
+                  "quantized_moe_sigmoid_amd/csrc/select_impl.h", "quantized_moe_sigmoid_amd/csrc/ffn_gemv_w4.hip",
+                  "quantized_moe_sigmoid_amd/csrc/ffn_mfma.hip"]
 LOCAL_GROUP_MAX_P = 512         # batches above this many (token, expert) pairs take the grouped-GEMM path
 
 

@@ -97,6 +97,22 @@ constexpr int LOCAL_GROUP_MAX_P = 512;  // pairs a GEMV workgroup groups by itse
 // ---- launchers (host side, one per kernel family); return hipError_t
 hipError_t launch_q8_0(const float *x, int64_t rows, int32_t cols, int8_t *q, float *d, hipStream_t s);
 
+// The router's selection step: partials in, route out (router.hip select kernels;
+// with part set in FfnArgs::sel, the decode gate/up GEMVs select the route themselves)
+struct SelectArgs {
+  const double *part;  // K-split logit partials [ksplit][T][E]
+  int ksplit, T, E, G, Gk, k;
+  float rsf;
+  float topp;  // 0: plain top-k; else adaptive expert top-p
+  const float *bias;
+  int32_t *idx;    // [T][k] out
+  float *w;        // [T][k] out
+  const float *x;  // quantised into xq/xd when xq != nullptr (select_kernel only)
+  int H;
+  int8_t *xq;
+  float *xd;
+};
+
 struct RouteLaunch {
   const coli_moe_cfg *cfg;
   const float *x;
@@ -109,7 +125,10 @@ struct RouteLaunch {
   int8_t *xq;        // quantise x into xq/xd in the selection kernel when non-null
   float *xd;
 };
-hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid);
+// Logits, then the selection; with `fused` set and route_fusable, the selection is
+// left to the gate/up GEMV: *fused receives its arguments (else part = nullptr).
+hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid, SelectArgs *fused = nullptr);
+bool route_fusable(const coli_moe_cfg &c, int32_t T, int32_t ks);
 hipError_t launch_group(const coli_moe_cfg &c, const int32_t *idx, int32_t T, int32_t *cnt, int32_t *off,
                         int32_t *perm, int32_t *active, int32_t *nact, hipStream_t s);
 bool group_supported(int P, int E);
@@ -130,6 +149,9 @@ struct FfnArgs {
   float *ypair;       // [P+T][H]
   float *tap;         // test builds (COLI_TAPS) only: [P+T][2F] pre-SiLU g | u per output row
   int32_t *redo;      // MXFP4 grouped GEMM: per work item, 1 = its scales need the integer path
+  // gate/up GEMVs only: with sel.part set, every workgroup selects the route from the
+  // logit partials itself (idx is then sel.idx, written by one workgroup)
+  SelectArgs sel;
 };
 
 // Test builds (compiled with COLI_TAPS) record the gate and up values of every output

@@ -104,7 +104,7 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
                        const float *topk_w, const int32_t *off, const int32_t *perm, const int32_t *active,
                        const int32_t *nact, const int32_t *local_idx, float *out, void *ws, const WsLayout &L,
                        hipStream_t s, hipEvent_t *ev, bool quantize_x, float *tap = nullptr, bool shared = true,
-                       bool combine = true) {
+                       bool combine = true, const SelectArgs *fsel = nullptr) {
   int st;
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
   if (quantize_x && (st = dev(launch_q8_0(x, T, c.hidden, at<int8_t>(ws, L.xq), at<float>(ws, L.xd), s))))
@@ -141,7 +141,9 @@ static int ffn_enqueue(const coli_moe_cfg &c, const coli_moe_weights &w, const f
   int32_t *ntiles = at<int32_t>(ws, L.ntiles);
   if (gemm && (st = dev(launch_plan(a, tiles, ntiles, gmax, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[1], s)))) return st;
+  if (fsel && !gemm) a.sel = *fsel;  // the gate/up GEMV selects the route (local_idx is its output)
   if ((st = dev(gemm ? launch_mfma_gateup(c.wfmt, a, tiles, ntiles, gmax, s) : launch_gateup(c.wfmt, a, s)))) return st;
+  a.sel = SelectArgs{};
   if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
   if ((st = dev(gemm ? launch_mfma_down(c.wfmt, a, tiles, ntiles, gmax, s) : launch_down(c.wfmt, a, s)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[3], s)))) return st;
@@ -250,12 +252,14 @@ static int layer_impl(const coli_moe_cfg *cfg, const coli_moe_weights *w, const 
   r.xd = at<float>(ws, L.xd);
   // decode-sized batches: every GEMV workgroup groups the route itself
   const bool local = (int64_t)T * cfg->top_k <= LOCAL_GROUP_MAX_P;
+  // small decode batches: the gate/up GEMV selects the route itself (fsel.part set)
+  SelectArgs fsel{};
   if (ev && (st = dev(hipEventRecord(ev[0], s)))) return st;
-  if ((st = dev(launch_route(r, s, ev ? ev[1] : nullptr)))) return st;
+  if ((st = dev(launch_route(r, s, ev ? ev[1] : nullptr, local ? &fsel : nullptr)))) return st;
   if (ev && (st = dev(hipEventRecord(ev[2], s)))) return st;
   if (!local && (st = dev(launch_group(*cfg, idx, T, cnt, off, perm, act, nact, s)))) return st;
   return ffn_enqueue(*cfg, *w, x, T, tw, off, perm, act, nact, local ? idx : nullptr, out, ws, L, s,
-                     ev ? ev + 3 : nullptr, false, tap);
+                     ev ? ev + 3 : nullptr, false, tap, true, true, fsel.part ? &fsel : nullptr);
 }
 
 // ---- fixed device scratch of the allocation-free entry point --------------------

@@ -32,9 +32,11 @@
 // Down epilogue: y fp32 rows, written per token as 32 consecutive floats.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "coli_internal.h"
+#include "select_impl.h"
 
 namespace coli {
 
@@ -283,8 +285,14 @@ struct SlotLds {
   int pairs[LOCAL_GROUP_MAX_P];
 };
 
+//
+// FUSE (gate/up kernels): with a.sel.part set, the workgroup first selects the route
+// itself from the logit partials (fused_route; its LDS and the route in the dynamic
+// LDS `dyn`, sized by fused_lds_bytes); the workgroup of the first routed slot's first
+// tile stores it to a.sel.idx / a.sel.w. The shared expert's workgroups need no route.
+template <bool FUSE = false>
 __device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, SlotLds &L, int &e, int &n, int &beg,
-                                             bool &shared) {
+                                             bool &shared, char *dyn = nullptr) {
   if (a.has_shared && slot == 0) {
     e = a.E;
     n = a.T;
@@ -305,6 +313,14 @@ __device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, SlotLds
   beg = 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int P = a.T * a.k;
+  const int *rt = nullptr;  // route selected in this workgroup (LDS)
+  if constexpr (FUSE) {
+    if (a.sel.part != nullptr) {
+      int *r = reinterpret_cast<int *>(dyn + fused_route_lds(a.T, a.E));
+      fused_route(a.sel, dyn, r, blockIdx.x == 0 && slot == a.has_shared);
+      rt = r;
+    }
+  }
   if (tid < 64) {
     constexpr int QD = LOCAL_GROUP_MAX_P / 64;
     int ev[QD];
@@ -313,7 +329,7 @@ __device__ __forceinline__ bool resolve_slot(const FfnArgs &a, int slot, SlotLds
       const int p = lane + 64 * i;
       ev[i] = -1;
       if (p < P) {
-        const int v = a.idx[p];
+        const int v = (FUSE && rt) ? rt[p] : a.idx[p];
         ev[i] = ((unsigned)v < (unsigned)a.E) ? v : -1;
       }
     }
@@ -443,9 +459,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   constexpr int BPC = Fmt<WB>::BPC;
 
   __shared__ SlotLds SL;
+  extern __shared__ __align__(16) char smem[];
   int e, n, beg;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+  if (!resolve_slot<MODE == MODE_GATEUP>(a, blockIdx.y, SL, e, n, beg, shared, smem)) return;
 
   const int K = (MODE == MODE_GATEUP) ? a.H : a.F;       // inputs per row
   const int NROWS = (MODE == MODE_GATEUP) ? a.F : a.H;   // output rows per matrix
@@ -469,7 +486,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(FfnArgs a) {
   const void *gsc0 = gs_base<WB>(a.scales, (MODE == MODE_GATEUP) ? se : se + 2 * ngh);
   const void *gsc1 = gs_base<WB>(a.scales, se + ngh);
 
-  extern __shared__ __align__(16) char smem[];
   int8_t *xs = reinterpret_cast<int8_t *>(smem);                      // [NT][K]
   float *xds = reinterpret_cast<float *>(smem + NT * K);              // [NT][nkb]
   float *obuf = reinterpret_cast<float *>(xds + NT * nkb);            // [NT][32]
@@ -830,9 +846,10 @@ __global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void 
   static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
 
   __shared__ SlotLds SL;
+  extern __shared__ __align__(16) char smem[];
   int e, n, beg;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+  if (!resolve_slot<MODE == MODE_GATEUP>(a, blockIdx.y, SL, e, n, beg, shared, smem)) return;
 
   const int K = (MODE == MODE_GATEUP) ? a.H : a.F;
   const int nkb = K / QK;
@@ -840,7 +857,6 @@ __global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void 
   const int64_t rbh = row_bytes(WB, a.H);
   const float *sc = a.scales + (int64_t)e * a.scale_stride;
 
-  extern __shared__ __align__(16) char smem[];
   FastCtx c;
   c.mat0 = (MODE == MODE_GATEUP) ? blob : blob + 2 * (int64_t)a.F * rbh;
   c.mat1 = blob + (int64_t)a.F * rbh;
@@ -973,9 +989,10 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(FfnArgs a) {
 
   __shared__ SlotLds SL;
   __shared__ float obuf[NMAT][NTC][TILE];
+  extern __shared__ __align__(16) char smem[];  // fused route only
   int e, n = 0, beg = 0;
   bool shared;
-  if (!resolve_slot(a, blockIdx.y, SL, e, n, beg, shared)) return;
+  if (!resolve_slot<MODE == MODE_GATEUP>(a, blockIdx.y, SL, e, n, beg, shared, smem)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rs = lane / LPR, sub = lane % LPR;
@@ -1212,13 +1229,23 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
 
   float s0 = 0.0f, s1 = 0.0f, s0n = 0.0f, s1n = 0.0f;
 
+  // the route: selected here from the logit partials (gate/up with a.sel.part set;
+  // the first workgroup stores it for the kernels that follow), else loaded
+  bool fused = false;
+  if constexpr (MODE == MODE_GATEUP) {
+    if (a.sel.part != nullptr) {
+      extern __shared__ __align__(16) char smem[];
+      fused_route(a.sel, smem, L.route, b == 0);
+      fused = true;
+    }
+  }
   // the hit experts, ascending (wavefront 0); the route loads go out together
   if (wv == 0) {
     int ev[QD];
 #pragma unroll
     for (int i = 0; i < QD; i++) {
       const int p = lane + 64 * i;
-      ev[i] = (p < P) ? a.idx[p] : -1;
+      ev[i] = (p < P) ? (fused ? L.route[p] : a.idx[p]) : -1;
     }
 #pragma unroll
     for (int i = 0; i < QD; i++) {
@@ -1395,6 +1422,13 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(FfnArgs a) {
   }
 }
 
+// dynamic LDS of a gate/up launch that selects the route itself: fused_route's, and
+// (with_route) the route of the batch
+static size_t fused_lds_bytes(const FfnArgs &a, bool with_route) {
+  if (a.sel.part == nullptr) return 0;
+  return fused_route_lds(a.T, a.E) + (with_route ? (size_t)a.T * a.k * sizeof(int) : 0);
+}
+
 // resident workgroups of a kernel on the current device (cached per device)
 template <typename Kern>
 static int resident_groups(Kern k, int threads) {
@@ -1425,7 +1459,7 @@ static hipError_t launch_pipe(const FfnArgs &a, int nrows, hipStream_t s) {
   if (res <= 0) return hipErrorNotSupported;
   const int64_t units = (int64_t)(a.has_shared + min(a.E, a.T * a.k)) * (nrows / TILE);
   const int grid = (int)(units < res ? units : res);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), fused_lds_bytes(a, false), s, a);
   return hipGetLastError();
 }
 
@@ -1442,10 +1476,11 @@ static hipError_t launch_reg(const FfnArgs &a, int nrows, int slots, hipStream_t
   // small batches)
   const bool dense = (int64_t)a.T * a.k >= 2 * (int64_t)a.E;  // most experts hit (about 86% or more)
   const dim3 grid(nrows / TILE, slots);
+  const size_t lds = fused_lds_bytes(a, true);
   if (MODE == MODE_GATEUP && dense)
-    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 2>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_reg_kernel<WB, LPR, MODE, WR, 1>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1466,8 +1501,9 @@ static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int 
   // per SIMD for the int4 gate/up instantiation), which matters more than reloading a
   // tile's weights from L2 for the rare expert with more than two tokens
   const int ntmax = min(2, a.T);
-  const size_t lds = (size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(float) + (size_t)NMAT * 8 * TILE * sizeof(float) +
-                     16 * sizeof(int);
+  const size_t lds = std::max((size_t)ntmax * K + (size_t)ntmax * (K / QK) * sizeof(float) +
+                                  (size_t)NMAT * 8 * TILE * sizeof(float) + 16 * sizeof(int),
+                              fused_lds_bytes(a, true));
   dim3 grid(nrows / TILE, slots_grid.y);
   hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR, GS>), grid, dim3(256), lds, s, a, ntmax);
   return hipGetLastError();
@@ -1508,8 +1544,9 @@ static hipError_t launch_mode(const FfnArgs &a, hipStream_t s) {
     if (r != hipErrorNotSupported) return r;
   }
   dim3 grid(NROWS / GEMV_ROWS, slots);
-  const size_t lds = (size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(float) +
-                     (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int);
+  const size_t lds = std::max((size_t)GEMV_NT * K + (size_t)GEMV_NT * nkb * sizeof(float) +
+                                  (size_t)GEMV_NT * GEMV_ROWS * sizeof(float) + 2 * GEMV_NT * sizeof(int),
+                              fused_lds_bytes(a, true));
   switch (lpr) {
 #define COLI_LPR_CASE(L) \
   case L: hipLaunchKernelGGL((gemv_kernel<WB, L, MODE, GS>), grid, dim3(256), lds, s, a); break;

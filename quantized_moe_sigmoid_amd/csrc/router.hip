@@ -19,12 +19,14 @@
 //     the 2 x T fp64 partial sums of a wavefront are folded with a reduce-scatter.
 //   logits_mfma_kernel (T > 16): fp64 MFMA GEMM, K-split; logits_kernel (T <= 16
 //     with H not a multiple of 256): LDS-tiled fp64 vector GEMM, K-split.
-//   select_kernel: one workgroup per token quantises the token's x (Q8_0), sums
-//     the K-split partials in a fixed order (deterministic) and performs the
-//     group-limited top-k as rank computations over LDS.
-#include <type_traits>
-
+//   select_kernel: one workgroup per token quantises the token's x (Q8_0) unless
+//     the logits kernel did, sums the K-split partials in a fixed order
+//     (deterministic) and performs the group-limited top-k as rank counts over
+//     LDS spread over the workgroup (sel_block, select_impl.h). For one decode
+//     token the gate/up GEMV runs the same selection itself instead
+//     (route_fusable).
 #include "q8_0_impl.h"
+#include "select_impl.h"
 
 namespace coli {
 
@@ -44,38 +46,6 @@ __device__ __forceinline__ double dpp_partner_d(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, 0xF, 0xF, false);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// The value that lane l ^ O holds, as a register exchange (no LDS round trip): the
-// permlane swaps for O = 32 and 16, the DPP permutes of dpp_partner_d for O <= 8,
-// whose partners for O = 8 and 4 are l ^ 15 and l ^ 7 (the row mirrors). {1, 2, 7, 15}
-// spans the 16 lanes of a row as {1, 2, 4, 8} does, so a butterfly over O = 1 .. G/2
-// (G a power of two) still combines every lane of each aligned group of G lanes.
-template <int O>
-__device__ __forceinline__ uint32_t partner_u(uint32_t v) {
-  if constexpr (O == 32 || O == 16) {
-    const auto r = (O == 32) ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
-                             : __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (__lane_id() & O) ? r[0] : r[1];
-  } else {
-    constexpr int ctrl = (O == 8) ? 0x140 : (O == 4) ? 0x141 : (O == 2) ? 0x4E : 0xB1;
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
-  }
-}
-
-template <int O>
-__device__ __forceinline__ double partner_d(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = partner_u<O>((uint32_t)b), hi = partner_u<O>((uint32_t)(b >> 32));
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// lane j's value (j wave-uniform), through scalar registers
-__device__ __forceinline__ double lane_d(double v, int j) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
@@ -328,90 +298,16 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const float *__restric
 }
 
 // ------------------------------------------------------------------ selection
-struct SelectArgs {
-  const double *part;
-  int ksplit, T, E, G, Gk, k;
-  float rsf;
-  float topp;  // 0: plain top-k; else adaptive expert top-p
-  const float *bias;
-  int32_t *idx;
-  float *w;
-  const float *x;  // quantised into xq/xd when xq != nullptr
-  int H;
-  int8_t *xq;
-  float *xd;
-};
-
-constexpr int SEL_NT = 256;  // threads per token
-
-// (v, i) ranks before (v2, i2): larger value first, then lower index
-__device__ __forceinline__ bool before(double v2, int i2, double v, int i) { return v2 > v || (v2 == v && i2 < i); }
-
-// number of entries j in [lo, lo + cnt) of (val[j], id(j)) that rank before (v, i); the
-// LDS reads are unrolled so that several are in flight
-template <typename IdOf>
-__device__ __forceinline__ int count_before(const double *val, int lo, int cnt, double v, int i, IdOf id) {
-  int r = 0;
-#pragma unroll 8
-  for (int j = lo; j < lo + cnt; j++) r += before(val[j], id(j), v, i) ? 1 : 0;
-  return r;
-}
-
-// The K-split logit partials of expert e (clamped: every load is valid, values past
-// E or ksplit are never used), first PK of them into registers
-template <int PK>
-__device__ __forceinline__ void load_partials(const SelectArgs &a, int t, int e, double (&pv)[PK]) {
-  const int ec = min(e, a.E - 1);
-#pragma unroll
-  for (int j = 0; j < PK; j++) pv[j] = a.part[((int64_t)min(j, a.ksplit - 1) * a.T + t) * a.E + ec];
-}
-
-// z of expert e: the partials summed in split order (the first PK from registers, the
-// rest loaded eight at a time)
-template <int PK>
-__device__ __forceinline__ double sum_partials(const SelectArgs &a, int t, int e, const double (&pv)[PK]) {
-  double z = 0.0;
-#pragma unroll
-  for (int j = 0; j < PK; j++)
-    if (j < a.ksplit) z += pv[j];
-  const double *pp = a.part + (int64_t)t * a.E + e;
-  const int64_t stride = (int64_t)a.T * a.E;
-  for (int k0 = PK; k0 < a.ksplit; k0 += 8) {
-    double v[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = (k0 + j < a.ksplit) ? pp[(k0 + j) * stride] : 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-      if (k0 + j < a.ksplit) z += v[j];
-  }
-  return z;
-}
-
-// One workgroup per token. Every step is a rank computation over LDS:
-//   c_e in LDS; the rank of e inside its group (c desc, lower index first) gives
-//   the two best values of each group, whose sum is the group score; the rank of a
-//   group among the group scores decides whether it is kept. An expert with k or
-//   more better experts in its own group cannot be among the k best, so only the
-//   experts of kept groups with in-group rank below k are candidates; the rank of
-//   a candidate among the candidates is its rank among all kept experts (every
-//   expert ranked before a selected one is a candidate), hence its output slot
-//   when below k. With one group the in-group rank already is the slot. Ranks are
-//   exact (the index breaks every tie).
-// The token's row of x is quantised (Q8_0) first, by the whole workgroup.
+// One workgroup per token: the token's row of x is quantised (Q8_0) first when the
+// logits kernel has not done it, the K-split partials are summed in a fixed order
+// (deterministic) into s and c in LDS, and the whole workgroup selects (sel_block:
+// group-limited top-k as rank counts over LDS).
 template <int EPT>
 __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
-  __shared__ double cs[SEL_NT * EPT];
-  __shared__ double cand_c[SEL_NT * EPT];
-  __shared__ int cand_e[SEL_NT * EPT];
-  __shared__ double cand_s[SEL_NT * EPT];
-  __shared__ double gtop[64][2];
-  __shared__ double gsc[64];
-  __shared__ int gkeep[64];
-  __shared__ int sel_e[64];
-  __shared__ double sel_s[64];
-  __shared__ int ncand;
+  __shared__ double cs[SEL_NT * EPT], ss[SEL_NT * EPT];
+  __shared__ SelBlockLds<EPT> L;
   const int t = blockIdx.x, tid = threadIdx.x;
-  const int E = a.E, G = a.G, k = a.k, m = E / G;
+  const int E = a.E;
 
   // the K-split partials of this thread's experts, loaded before the x work so
   // that both round trips overlap (up to PK splits in registers, the rest later)
@@ -451,265 +347,19 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
     for (int b0 = XQ * (SEL_NT / 8); b0 < nblk; b0 += XQ * (SEL_NT / 8)) chunk(b0);
   }
 
-  double s[EPT], c[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
     const int e = tid + SEL_NT * i;
-    s[i] = 0.0;
-    c[i] = -INFINITY;
-    if (e < E) {
-      const double z = sum_partials(a, t, e, pv[i]);
-      s[i] = 1.0 / (1.0 + exp(-z));
-      c[i] = s[i] + (double)a.bias[e];
-      cs[e] = c[i];
-    }
-  }
-  if (tid < 64) sel_e[tid] = -1;
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-
-  // rank of each expert inside its group
-  int rin[EPT];
-  auto self = [](int j) { return j; };
-#pragma unroll
-  for (int i = 0; i < EPT; i++) {
-    const int e = tid + SEL_NT * i;
-    rin[i] = 0x7fffffff;
-    if (e < E) {
-      rin[i] = count_before(cs, (e / m) * m, m, c[i], e, self);
-      if (G > 1 && rin[i] < 2) gtop[e / m][rin[i]] = c[i];
-    }
-  }
-  if (G == 1) {
-#pragma unroll
-    for (int i = 0; i < EPT; i++) {
-      const int e = tid + SEL_NT * i;
-      if (e < E && rin[i] < k) {
-        sel_e[rin[i]] = e;
-        sel_s[rin[i]] = s[i];
-      }
-    }
-  } else {
-    __syncthreads();
-    if (tid < G) gsc[tid] = (m > 1) ? gtop[tid][0] + gtop[tid][1] : gtop[tid][0];
-    __syncthreads();
-    if (tid < G) gkeep[tid] = count_before(gsc, 0, G, gsc[tid], tid, self) < a.Gk;
-    __syncthreads();
-    // candidates: kept groups, in-group rank below k (slot order is free: ranks decide)
-#pragma unroll
-    for (int i = 0; i < EPT; i++) {
-      const int e = tid + SEL_NT * i;
-      if (e < E && rin[i] < k && gkeep[e / m]) {
-        const int q = atomicAdd(&ncand, 1);
-        cand_c[q] = c[i];
-        cand_s[q] = s[i];
-        cand_e[q] = e;
-      }
-    }
-    __syncthreads();
-    const int nc = ncand;
-    for (int q = tid; q < nc; q += SEL_NT) {
-      const int e = cand_e[q];
-      const int r = count_before(cand_c, 0, nc, cand_c[q], e, [&](int j) { return cand_e[j]; });
-      if (r < k) {
-        sel_e[r] = e;
-        sel_s[r] = cand_s[q];
-      }
-    }
+    if (e < E) sel_score(a, t, e, pv[i], ss[e], cs[e]);
   }
   __syncthreads();
-  if (tid < k) {
-    double S = 0.0;
-    for (int j = 0; j < k; j++) S += sel_s[j];
-    int kept = k;
-    if (a.topp > 0.0f) {
-      // adaptive top-p: the shortest prefix of the slots whose scores reach topp * S;
-      // its sum (same order) renormalises the kept weights
-      const double target = (double)a.topp * S;
-      double cum = 0.0;
-      for (int j = 0; j < k; j++) {
-        cum += sel_s[j];
-        if (cum >= target) {
-          kept = j + 1;
-          break;
-        }
-      }
-      S = cum;
-    }
-    int e = sel_e[tid];
-    float wt = (e >= 0) ? (float)((sel_s[tid] / S) * (double)a.rsf) : 0.0f;
-    if (tid >= kept) {
-      e = -1;
-      wt = 0.0f;
-    }
-    a.idx[(int64_t)t * k + tid] = e;
-    a.w[(int64_t)t * k + tid] = wt;
+  int e;
+  float wt;
+  sel_block<EPT>(a, cs, ss, L, e, wt);
+  if (tid < a.k) {
+    a.idx[(int64_t)t * a.k + tid] = e;
+    a.w[(int64_t)t * a.k + tid] = wt;
   }
-}
-
-// Decode-sized batches (x already quantised by the logits kernel) whose experts split
-// evenly over the 64 lanes of a wavefront: E = 64 EPL with EPL in {1, 2, 4, 8}, the
-// EPL experts of a lane inside one group, and a group on a power of two of lanes.
-// The same selection as select_kernel, with the same order (larger value first,
-// lower index on ties) at every step, so the result is identical:
-//   - the workgroup sums each expert's partials and writes s and c to LDS (one
-//     barrier); then a single wavefront works on its registers and lane exchanges:
-//   - a lane sorts its EPL experts; the two best c of a group are merged across the
-//     group's lanes by register exchanges (DPP, permlane swaps), and their sum is the
-//     group score;
-//   - a group is kept when fewer than Gk groups rank before its score;
-//   - the k slots are k rounds of a wavefront arg-max over the lanes' best remaining
-//     kept expert, the winner's lane dropping it: slot r holds the expert of rank r
-//     among the kept experts;
-//   - the weights are formed as in select_kernel (same sums in slot order).
-// Every lane exchange is a register permute (DPP, permlane swap) or a readlane: the
-// k arg-max rounds form a chain of 6 k dependent exchanges, which as LDS-routed
-// shuffles cost about 3.5 us at k = 8 and as register permutes a fraction of that.
-template <int EPL>
-__global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a) {
-  constexpr int E = 64 * EPL;
-  constexpr int EPT = (E + SEL_NT - 1) / SEL_NT;
-  constexpr int PK = (EPT == 1) ? 24 : 12;
-  __shared__ double cs[E], ss[E];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  double pv[EPT][PK];
-#pragma unroll
-  for (int i = 0; i < EPT; i++) load_partials(a, t, tid + SEL_NT * i, pv[i]);
-#pragma unroll
-  for (int i = 0; i < EPT; i++) {
-    const int e = tid + SEL_NT * i;
-    if (e < E) {
-      const double z = sum_partials(a, t, e, pv[i]);
-      const double sv = 1.0 / (1.0 + exp(-z));
-      ss[e] = sv;
-      cs[e] = sv + (double)a.bias[e];
-    }
-  }
-  __syncthreads();
-  if (tid >= 64) return;
-  const int lane = tid, G = a.G, k = a.k;
-  const int m = E / G;        // experts per group
-  const int lpg = m / EPL;    // lanes per group
-  double v[EPL];
-  int id[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; i++) {
-    id[i] = EPL * lane + i;
-    v[i] = cs[id[i]];
-  }
-  // the lane's experts, best first
-#pragma unroll
-  for (int p = 0; p + 1 < EPL; p++)
-#pragma unroll
-    for (int q = 0; q + 1 < EPL - p; q++)
-      if (before(v[q + 1], id[q + 1], v[q], id[q])) {
-        const double tv = v[q];
-        v[q] = v[q + 1];
-        v[q + 1] = tv;
-        const int ti = id[q];
-        id[q] = id[q + 1];
-        id[q + 1] = ti;
-      }
-  bool kept = true;
-  if (G > 1) {
-    // the group's two largest c on every lane of the group
-    double t1 = v[0], t2 = (EPL > 1) ? v[1] : -INFINITY;
-    auto merge = [&](auto o_tag) __attribute__((always_inline)) {
-      constexpr int O = decltype(o_tag)::value;
-      const double b1 = partner_d<O>(t1), b2 = partner_d<O>(t2);
-      const double lo = (b1 > t1) ? t1 : b1;
-      const double hi2 = (b2 > t2) ? b2 : t2;
-      t1 = (b1 > t1) ? b1 : t1;
-      t2 = (hi2 > lo) ? hi2 : lo;
-    };
-    if (lpg > 1) merge(std::integral_constant<int, 1>{});
-    if (lpg > 2) merge(std::integral_constant<int, 2>{});
-    if (lpg > 4) merge(std::integral_constant<int, 4>{});
-    if (lpg > 8) merge(std::integral_constant<int, 8>{});
-    if (lpg > 16) merge(std::integral_constant<int, 16>{});
-    if (lpg > 32) merge(std::integral_constant<int, 32>{});
-    const double score = (m > 1) ? t1 + t2 : t1;
-    const int g = lane / lpg;
-    int rank = 0;
-    for (int j = 0; j < G; j++) rank += before(lane_d(score, j * lpg), j, score, g) ? 1 : 0;
-    kept = rank < a.Gk;
-  }
-  if (!kept) {
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-      v[i] = -INFINITY;
-      id[i] = INT_MAX;
-    }
-  }
-  int my_e = -1;
-  for (int r = 0; r < k; r++) {
-    double bv = v[0];
-    int bi = id[0];
-    auto step = [&](auto o_tag) __attribute__((always_inline)) {
-      constexpr int O = decltype(o_tag)::value;
-      const double ov = partner_d<O>(bv);
-      const int oi = (int)partner_u<O>((uint32_t)bi);
-      if (before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    };
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    step(std::integral_constant<int, 4>{});
-    step(std::integral_constant<int, 8>{});
-    step(std::integral_constant<int, 16>{});
-    step(std::integral_constant<int, 32>{});
-    if (lane == r) my_e = bi;
-    if (id[0] == bi) {  // this lane's best was taken
-#pragma unroll
-      for (int i = 0; i + 1 < EPL; i++) {
-        v[i] = v[i + 1];
-        id[i] = id[i + 1];
-      }
-      v[EPL - 1] = -INFINITY;
-      id[EPL - 1] = INT_MAX;
-    }
-  }
-  const double s_me = (lane < k) ? ss[my_e] : 0.0;
-  double S = 0.0;
-  for (int j = 0; j < k; j++) S += lane_d(s_me, j);
-  int kept_n = k;
-  if (a.topp > 0.0f) {
-    // adaptive top-p, as in select_kernel
-    const double target = (double)a.topp * S;
-    double cum = 0.0;
-    for (int j = 0; j < k; j++) {
-      cum += lane_d(s_me, j);
-      if (cum >= target) {
-        kept_n = j + 1;
-        break;
-      }
-    }
-    S = cum;
-  }
-  if (lane < k) {
-    int e = my_e;
-    float wt = (float)((s_me / S) * (double)a.rsf);
-    if (lane >= kept_n) {
-      e = -1;
-      wt = 0.0f;
-    }
-    a.idx[(int64_t)t * k + lane] = e;
-    a.w[(int64_t)t * k + lane] = wt;
-  }
-}
-
-// select_wave_kernel's layout conditions; returns its EPL or 0
-static int wave_select_epl(int E, int G, bool x_done) {
-  if (!x_done || E % 64 || E > 512 || G <= 0 || E % G) return 0;
-  const int epl = E / 64;
-  if (epl & (epl - 1)) return 0;
-  const int m = E / G;
-  if (m % epl) return 0;
-  const int lpg = m / epl;
-  if (lpg & (lpg - 1)) return 0;
-  return epl;
 }
 
 // ------------------------------------------------------------------ host side
@@ -725,7 +375,19 @@ int32_t route_ksplit(const coli_moe_cfg &c, int32_t T) {
   return 1;
 }
 
-hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
+// Whether the decode gate/up GEMVs select this batch's route themselves: one token
+// (every workgroup repeats the selection, about 2 us at E = 64 and 4.5 us at E = 256
+// in a workgroup's timeline, against about 3 us that the selection launch and its
+// boundary cost; two tokens would double the repeated work), the decode logits kernel
+// runs (x quantised there), E <= 512, and the partials every workgroup reads (E *
+// ksplit doubles) stay small.
+constexpr int64_t FUSE_PART_BYTES = 64 << 10;
+bool route_fusable(const coli_moe_cfg &c, int32_t T, int32_t ks) {
+  if (T != 1 || c.hidden % 256 || c.top_k > LOCAL_GROUP_MAX_P || c.n_experts > 2 * SEL_NT) return false;
+  return (int64_t)c.n_experts * ks * 8 <= FUSE_PART_BYTES;
+}
+
+hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid, SelectArgs *fused) {
   const coli_moe_cfg &c = *r.cfg;
   const int E = c.n_experts, H = c.hidden, T = r.T;
   const int ks = r.ksplit;
@@ -764,14 +426,14 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid) {
   a.H = H;
   a.xq = x_done ? nullptr : r.xq;
   a.xd = r.xd;
-  if (T == 0) return hipSuccess;
-  switch (wave_select_epl(E, c.n_group, x_done)) {
-    case 1: hipLaunchKernelGGL(select_wave_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
-    case 2: hipLaunchKernelGGL(select_wave_kernel<2>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
-    case 4: hipLaunchKernelGGL(select_wave_kernel<4>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
-    case 8: hipLaunchKernelGGL(select_wave_kernel<8>, dim3(T), dim3(SEL_NT), 0, s, a); return hipGetLastError();
-    default: break;
+  if (fused) {
+    *fused = SelectArgs{};
+    if (x_done && route_fusable(c, T, ks)) {  // the selection runs in the gate/up GEMV
+      *fused = a;
+      return hipSuccess;
+    }
   }
+  if (T == 0) return hipSuccess;
   if (E <= SEL_NT)
     hipLaunchKernelGGL(select_kernel<1>, dim3(T), dim3(SEL_NT), 0, s, a);
   else if (E <= 2 * SEL_NT)

@@ -131,9 +131,11 @@ def test_route_ties_lowest_index(q, orc):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
-# The wavefront selection kernel serves batches of up to 16 tokens with H a multiple of
-# 256 and E = 64 EPL (EPL 1, 2, 4, 8), a lane's experts in one group and a group on a
-# power of two of lanes. Every layout it handles, against the oracle.
+# Decode-sized batches (H a multiple of 256, x quantised by the logits kernel): the
+# selection splits each expert's rank count over several threads when E < 256 (by the
+# group size), places the candidates of the kept groups by group rank, and splits the
+# candidates' rank counts too. Groups of one expert, of 8 to 256 experts, one group,
+# k = 64 and E = 512 (two experts per thread), against the oracle.
 WAVE_CASES = [  # E, G, Gk, k, T, topp
     (64, 1, 1, 8, 3, 0.0),        # one group
     (64, 64, 8, 4, 5, 0.0),       # one expert per group: the group score is c itself
@@ -163,7 +165,7 @@ def _route_both(q, orc, cfgd, inp, T):
 
 
 @pytest.mark.parametrize("E,G,Gk,k,T,topp", WAVE_CASES)
-def test_route_wave_select_bitexact(q, orc, E, G, Gk, k, T, topp):
+def test_route_decode_select_bitexact(q, orc, E, G, Gk, k, T, topp):
     cfgd = _cfg(hidden=256, n_experts=E, top_k=k, n_group=G, topk_group=Gk, rsf=2.5, topp=topp)
     inp = synth.layer_inputs(300 + E + G + k + T, 0, tokens=T, hidden=256, ffn=128, n_experts=E, has_shared=False,
                              wbits=4, with_blobs=False)
@@ -174,8 +176,8 @@ def test_route_wave_select_bitexact(q, orc, E, G, Gk, k, T, topp):
         assert (ridx < 0).any()  # the top-p cut removed slots in this batch
 
 
-def test_route_wave_select_ties(q, orc):
-    """Exact ties on the wavefront path: experts with identical router rows and equal bias,
+def test_route_decode_select_ties(q, orc):
+    """Exact ties at decode sizes: experts with identical router rows and equal bias,
     inside one group and across groups, and two groups identical as a whole (equal group
     scores): the lower index wins every tie, as in the oracle."""
     E, G = 128, 4
