@@ -108,6 +108,20 @@ __device__ __forceinline__ int count_before_n(const double *val, int first, int 
   return r;
 }
 
+// sum of v over each aligned group of P consecutive lanes (P a power of two <= 64),
+// in every lane of the group: a butterfly over the DPP partners l ^ 1, l ^ 2 (quad
+// permutes), l ^ 7, l ^ 15 (half-row and row mirrors), which pair the halves of groups
+// of 2, 4, 8 and 16 lanes, then lane shuffles for 32 and 64
+__device__ __forceinline__ int sum_lanes(int v, int P) {
+  if (P > 1) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  if (P > 2) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  if (P > 4) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  if (P > 8) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  if (P > 16) v += __shfl_xor(v, 16);
+  if (P > 32) v += __shfl_xor(v, 32);
+  return v;
+}
+
 // threads per item when SEL_NT threads share n items of `len` entries each: the
 // largest power of two P <= 64 with n * P <= SEL_NT that divides len
 __device__ __forceinline__ int sel_split(int n, int len) {
@@ -130,12 +144,12 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
   // in-group ranks: expert tid / P, part tid % P of its group's m entries (P = 1 when
   // a thread holds several experts)
   const int P = (EPT == 1) ? sel_split(E, m) : 1;
-  const int p = tid & (P - 1);
+  const int p = tid & (P - 1), lp = __builtin_ctz(P);
   int ex[EPT], rin[EPT];
   double cx[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
-    ex[i] = (EPT == 1) ? tid / P : tid + SEL_NT * i;
+    ex[i] = (EPT == 1) ? tid >> lp : tid + SEL_NT * i;
     rin[i] = 0;
     cx[i] = 0.0;
     if (ex[i] < E) {
@@ -143,7 +157,7 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
       const int n = m / P;
       rin[i] = count_before_n(cs, (ex[i] / m) * m + p * n, n, cx[i], ex[i], self);
     }
-    for (int o = 1; o < P; o <<= 1) rin[i] += __shfl_xor(rin[i], o);
+    rin[i] = sum_lanes(rin[i], P);
   }
   const bool lead = p == 0;
   if (G == 1) {
@@ -187,7 +201,7 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
     auto cid = [&](int j) { return L.cand_e[j]; };
     if (nc <= SEL_NT) {
       const int P2 = sel_split(nc, nc);
-      const int q = tid / P2, p2 = tid & (P2 - 1), n2 = nc / P2;
+      const int q = tid >> __builtin_ctz(P2), p2 = tid & (P2 - 1), n2 = nc / P2;
       int r = 0;
       double cq = 0.0;
       int eq = 0;
@@ -196,7 +210,7 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
         eq = L.cand_e[q];
         r = count_before_n(L.cand_c, p2 * n2, n2, cq, eq, cid);
       }
-      for (int o = 1; o < P2; o <<= 1) r += __shfl_xor(r, o);
+      r = sum_lanes(r, P2);
       if (q < nc && p2 == 0 && r < k) {
         L.sel_e[r] = eq;
         L.sel_s[r] = L.cand_s[q];
