@@ -181,7 +181,10 @@ int coli_moe_ffn(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float
                  void *workspace, size_t ws_bytes, void *stream);
 
 /* The whole layer on one stream: route, group, FFN, combine. topk_idx_opt and
- * topk_w_opt ([T][k]) receive the route when non-NULL. */
+ * topk_w_opt ([T][k]) receive the route when non-NULL. For one token (T = 1, hidden a
+ * multiple of 256, n_experts <= 512) the route's selection runs inside the gate/up
+ * kernel instead of a kernel of its own; the route and the output are the same bit for
+ * bit as coli_moe_route followed by coli_moe_group and coli_moe_ffn. */
 int coli_moe_layer(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T, float *out,
                    int32_t *topk_idx_opt, float *topk_w_opt, void *workspace, size_t ws_bytes, void *stream);
 
@@ -207,7 +210,10 @@ int coli_moe_layer_noalloc(const coli_moe_cfg *cfg, const coli_moe_weights *w, c
 /* Measurement variant of coli_moe_layer: events[i] (hipEvent_t passed as void*,
  * created by the caller) is recorded on `stream` just before stage i and
  * events[n_stages] after the last stage; n_events must be coli_moe_num_stages()+1.
- * Results are identical to coli_moe_layer. */
+ * A stage run inside another stage's kernel is empty (its two events back to back:
+ * "group" below 513 (token, expert) pairs, "quantize_x" always (x is quantised by
+ * the logits or the selection kernel), "route_select" for one token, whose selection
+ * is timed in "ffn_gate_up"). Results are identical to coli_moe_layer. */
 int coli_moe_layer_profiled(const coli_moe_cfg *cfg, const coli_moe_weights *w, const float *x, int32_t T,
                             float *out, void *workspace, size_t ws_bytes, void *stream, void **events,
                             int32_t n_events);
