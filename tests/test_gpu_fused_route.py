@@ -148,3 +148,29 @@ def test_fused_route_batch_invariant_and_repeatable(q):
         assert np.array_equal(idx1[0], idx4[t])
         assert np.array_equal(tw1[0].view(np.uint32), tw4[t].view(np.uint32))
         assert np.array_equal(out1[0].view(np.uint32), out4[t].view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_profiled_layer_matches_layer(q, T):
+    """coli_moe_layer_profiled runs the same launches as coli_moe_layer, with events
+    between the stages (with one token the selection inside the gate/up GEMV): same
+    output bits, and every stage's events complete."""
+    import torch
+    cfgd = _cfg(hidden=2048, ffn=256, has_shared=True)
+    inp = _inputs(cfgd, T, 61 + T)
+    w = gu.upload_layer(inp)
+    out, _, _ = gu.run_layer(cfgd, w, inp["x"])
+    cfg = q.make_cfg(**cfgd)
+    d = gu.dev()
+    x = gu.to_dev(inp["x"])
+    out2 = torch.empty((T, cfgd["hidden"]), dtype=torch.float32, device=d)
+    ns = q.num_stages()
+    names = [q.stage_name(i) for i in range(ns)]
+    ev = q.TimingEvents(ns + 1)
+    stream = torch.cuda.current_stream(d)
+    q.layer_profiled(cfg, w, x, out2, q.alloc_workspace(cfg, T, d), ev, stream=stream)
+    stream.synchronize()
+    assert np.array_equal(out.view(np.uint32), out2.cpu().numpy().view(np.uint32))
+    for i in range(ns):
+        assert ev.elapsed_ms(i, i + 1) >= 0.0, names[i]
+    ev.close()

@@ -49,7 +49,7 @@ def _both(q, cfgd, w, x_np):
 
 @pytest.mark.parametrize("cfgd,Ts", [
     (dict(hidden=2048, ffn=1024, n_experts=64, top_k=8, n_group=1, topk_group=1, rsf=1.0, has_shared=False,
-          wbits=4), (16, 3)),
+          wbits=4), (16, 3, 1)),  # the last call selects its route inside the gate/up GEMV
     (dict(hidden=256, ffn=128, n_experts=16, top_k=4, n_group=4, topk_group=2, rsf=2.5, has_shared=True,
           wbits=4), (200, 150, 5)),   # grouped GEMM (800, 600 pairs), then a decode batch
     (dict(hidden=6144, ffn=2048, n_experts=16, top_k=8, n_group=8, topk_group=4, rsf=2.5, has_shared=True,
