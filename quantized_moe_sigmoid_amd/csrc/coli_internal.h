@@ -111,6 +111,11 @@ struct SelectArgs {
   int H;
   int8_t *xq;
   float *xd;
+  // the selection's shape, worked out on the host (sel_plan): m = E / G experts per
+  // group (gshift = log2 m when m is a power of two, else -1); P threads per expert
+  // splitting its group's m entries into n1 each; kk = min(k, m) candidates per kept
+  // group, nc = Gk * kk in all; P2 threads per candidate, n2 candidates each
+  int m, gshift, P, n1, kk, nc, P2, n2;
 };
 
 struct RouteLaunch {

@@ -426,6 +426,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid, Sel
   a.H = H;
   a.xq = x_done ? nullptr : r.xq;
   a.xd = r.xd;
+  sel_plan(a);
   if (fused) {
     *fused = SelectArgs{};
     if (x_done && route_fusable(c, T, ks)) {  // the selection runs in the gate/up GEMV

@@ -1,7 +1,7 @@
 // select_impl.h — the expert selection of the sigmoid noaux_tc router as device code,
-// shared by the selection kernels (router.hip) and by the decode gate/up GEMVs that
-// select the route themselves (ffn_gemv_impl.h), so that both give the same ids and
-// weights bit for bit.
+// shared by the selection kernel (router.hip) and by the decode gate/up GEMVs that
+// select a one-token route themselves (ffn_gemv_impl.h), so that both give the same ids
+// and weights bit for bit.
 //
 // colibri-strix README, "What's implemented", router item (DeepSeek-V3-style sigmoid
 // noaux_tc router with routed_scaling_factor). From the fp64 logits z_e (summed from
@@ -124,11 +124,28 @@ __device__ __forceinline__ int sum_lanes(int v, int P) {
 
 // threads per item when SEL_NT threads share n items of `len` entries each: the
 // largest power of two P <= 64 with n * P <= SEL_NT that divides len
-__device__ __forceinline__ int sel_split(int n, int len) {
+__host__ __device__ inline int sel_split(int n, int len) {
   int P = 1;
   while (P < 64 && n * (2 * P) <= SEL_NT && len % (2 * P) == 0) P *= 2;
   return P;
 }
+
+// The selection's shape for E experts in G groups, k slots, Gk kept groups (host side,
+// once per launch; the kernels read it from the arguments instead of dividing)
+inline void sel_plan(SelectArgs &a) {
+  const int m = a.E / a.G;
+  a.m = m;
+  a.gshift = (m & (m - 1)) ? -1 : __builtin_ctz(m);
+  a.P = (a.E <= SEL_NT) ? sel_split(a.E, m) : 1;
+  a.n1 = m / a.P;
+  a.kk = a.k < m ? a.k : m;
+  a.nc = a.Gk * a.kk;
+  a.P2 = (a.nc <= SEL_NT) ? sel_split(a.nc, a.nc) : 1;
+  a.n2 = a.nc / a.P2;
+}
+
+// group of expert e
+__device__ __forceinline__ int sel_group(const SelectArgs &a, int e) { return a.gshift >= 0 ? e >> a.gshift : e / a.m; }
 
 // cs, ss: c and s of the token's E <= SEL_NT * EPT experts in LDS, visible to every
 // thread. Every thread of the workgroup calls it; thread j < k returns slot j's expert
@@ -138,24 +155,24 @@ template <int EPT>
 __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs, const double *ss,
                                           SelBlockLds<EPT> &L, int &e_out, float &w_out) {
   const int tid = threadIdx.x;
-  const int E = a.E, G = a.G, k = a.k, m = E / G;
+  const int E = a.E, G = a.G, k = a.k, m = a.m;
   auto self = [](int j) { return j; };
   if (tid < 64) L.sel_e[tid] = -1;
   // in-group ranks: expert tid / P, part tid % P of its group's m entries (P = 1 when
   // a thread holds several experts)
-  const int P = (EPT == 1) ? sel_split(E, m) : 1;
+  const int P = (EPT == 1) ? a.P : 1, n1 = (EPT == 1) ? a.n1 : m;
   const int p = tid & (P - 1), lp = __builtin_ctz(P);
-  int ex[EPT], rin[EPT];
+  int ex[EPT], rin[EPT], gx[EPT];
   double cx[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; i++) {
     ex[i] = (EPT == 1) ? tid >> lp : tid + SEL_NT * i;
+    gx[i] = sel_group(a, ex[i]);
     rin[i] = 0;
     cx[i] = 0.0;
     if (ex[i] < E) {
       cx[i] = cs[ex[i]];
-      const int n = m / P;
-      rin[i] = count_before_n(cs, (ex[i] / m) * m + p * n, n, cx[i], ex[i], self);
+      rin[i] = count_before_n(cs, gx[i] * m + p * n1, n1, cx[i], ex[i], self);
     }
     rin[i] = sum_lanes(rin[i], P);
   }
@@ -171,7 +188,7 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
   } else {
 #pragma unroll
     for (int i = 0; i < EPT; i++)
-      if (lead && ex[i] < E && rin[i] < 2) L.gtop[ex[i] / m][rin[i]] = cx[i];
+      if (lead && ex[i] < E && rin[i] < 2) L.gtop[gx[i]][rin[i]] = cx[i];
     __syncthreads();
     // group scores and their ranks (lane g of wavefront 0 for group g)
     if (tid < 64) {
@@ -183,11 +200,11 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
       if (g < G) L.gpos[g] = (r < a.Gk) ? r : -1;
     }
     __syncthreads();
-    const int kk = min(k, m);
+    const int kk = a.kk;
 #pragma unroll
     for (int i = 0; i < EPT; i++)
       if (lead && ex[i] < E && rin[i] < kk) {
-        const int gp = L.gpos[ex[i] / m];
+        const int gp = L.gpos[gx[i]];
         if (gp >= 0) {
           const int q = gp * kk + rin[i];
           L.cand_c[q] = cx[i];
@@ -197,11 +214,11 @@ __device__ __forceinline__ void sel_block(const SelectArgs &a, const double *cs,
       }
     __syncthreads();
     // rank of each candidate among the nc candidates, P2 threads per candidate
-    const int nc = a.Gk * kk;
+    const int nc = a.nc;
     auto cid = [&](int j) { return L.cand_e[j]; };
     if (nc <= SEL_NT) {
-      const int P2 = sel_split(nc, nc);
-      const int q = tid >> __builtin_ctz(P2), p2 = tid & (P2 - 1), n2 = nc / P2;
+      const int P2 = a.P2, n2 = a.n2;
+      const int q = tid >> __builtin_ctz(P2), p2 = tid & (P2 - 1);
       int r = 0;
       double cq = 0.0;
       int eq = 0;
