@@ -15,8 +15,9 @@
 //
 // Kernels:
 //   logits_decode_kernel (T <= 16): 8 experts per workgroup and one K-chunk of
-//     x staged in LDS; every lane issues all its weight loads before the barrier;
-//     the 2 x T fp64 partial sums of a wavefront are folded with a reduce-scatter.
+//     x staged in LDS for 1, 4 or 8 tokens; every lane issues all its weight loads
+//     before the barrier; the 2 x TT fp64 partial sums of a wavefront are folded with
+//     a reduce-scatter.
 //   logits_mfma_kernel (T > 16): fp64 MFMA GEMM, K-split; logits_kernel (T <= 16
 //     with H not a multiple of 256): LDS-tiled fp64 vector GEMM, K-split.
 //   select_kernel: one workgroup per token quantises the token's x (Q8_0) unless
@@ -87,14 +88,20 @@ __device__ __forceinline__ void reduce_scatter_d(double *a, int lane, int &base)
 // When xq is set, the workgroups of each K chunk also quantise that chunk of x
 // (Q8_0, 32-value blocks, eight lanes per block) from the copy staged in LDS, 32
 // blocks per workgroup, so the selection kernel has no x work left.
-template <int NI>  // float4 per lane per row: kc = 256 * NI
+// TT tokens per workgroup (tokens TT z .. TT z + TT - 1 of blockIdx.z): the 2 TT sums of
+// a wavefront are folded with one reduce-scatter, so a one-token batch folds 2 sums,
+// not 32, and 16 tokens run as two slices of 8 over twice the workgroups.
+template <int NI, int TT>  // float4 per lane per row: kc = 256 * NI
 __global__ __launch_bounds__(256) void logits_decode_kernel(const float *__restrict__ x, const float *__restrict__ W,
                                                             int T, int E, int H, double *__restrict__ part,
                                                             int8_t *__restrict__ xq, float *__restrict__ xd) {
   constexpr int KC = 256 * NI;
-  __shared__ float4 xs[LD_TT * KC / 4];
+  constexpr int V = LD_EPW * TT;  // sums per lane
+  static_assert(V <= 64 && (V & (V - 1)) == 0, "sums per wavefront fold to lanes");
+  __shared__ float4 xs[TT * KC / 4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ks = blockIdx.y, k0 = ks * KC;
+  const int t0 = blockIdx.z * TT, nt = min(TT, T - t0);  // this workgroup's tokens
   const int e0 = blockIdx.x * (4 * LD_EPW) + wv * LD_EPW;
   // weight loads first (independent of the LDS staging)
   float4 w[LD_EPW][NI];
@@ -105,51 +112,51 @@ __global__ __launch_bounds__(256) void logits_decode_kernel(const float *__restr
     for (int i = 0; i < NI; i++)
       w[j][i] = reinterpret_cast<const float4 *>(W + (int64_t)e * H + k0)[i * 64 + lane];
   }
-  for (int i = tid; i < T * (KC / 4); i += 256) {
+  for (int i = tid; i < nt * (KC / 4); i += 256) {
     const int t = i / (KC / 4), c = i % (KC / 4);
-    xs[i] = reinterpret_cast<const float4 *>(x + (int64_t)t * H + k0)[c];
+    xs[i] = reinterpret_cast<const float4 *>(x + (int64_t)(t0 + t) * H + k0)[c];
   }
   __syncthreads();
   if (xq) {
     constexpr int BPT = KC / QK;  // blocks per token in this chunk
-    const int nq = T * BPT, sub = tid & 7;
+    const int nq = nt * BPT, sub = tid & 7;
     for (int q0 = blockIdx.x * 32; q0 < nq; q0 += gridDim.x * 32) {
       const int q = q0 + (tid >> 3);
       if (q < nq) {  // uniform over the eight lanes of a block
         const int t = q / BPT, b = q % BPT;
         uint32_t packed;
         const float d = q8_0_block8(xs[t * (KC / 4) + b * 8 + sub], packed);
-        reinterpret_cast<uint32_t *>(xq + (int64_t)t * H + k0)[b * 8 + sub] = packed;
-        if (sub == 0) xd[(int64_t)t * (H / QK) + k0 / QK + b] = d;
+        reinterpret_cast<uint32_t *>(xq + (int64_t)(t0 + t) * H + k0)[b * 8 + sub] = packed;
+        if (sub == 0) xd[(int64_t)(t0 + t) * (H / QK) + k0 / QK + b] = d;
       }
     }
   }
-  double acc[LD_EPW * LD_TT];
+  double acc[V];
 #pragma unroll
-  for (int i = 0; i < LD_EPW * LD_TT; i++) acc[i] = 0.0;
+  for (int i = 0; i < V; i++) acc[i] = 0.0;
 #pragma unroll
-  for (int t = 0; t < LD_TT; t++) {
-    if (t < T) {
+  for (int t = 0; t < TT; t++) {
+    if (t < nt) {
 #pragma unroll
       for (int i = 0; i < NI; i++) {
         const float4 xv = xs[t * (KC / 4) + i * 64 + lane];
 #pragma unroll
         for (int j = 0; j < LD_EPW; j++) {
-          double a = acc[j * LD_TT + t];
+          double a = acc[j * TT + t];
           a = fma((double)xv.x, (double)w[j][i].x, a);
           a = fma((double)xv.y, (double)w[j][i].y, a);
           a = fma((double)xv.z, (double)w[j][i].z, a);
           a = fma((double)xv.w, (double)w[j][i].w, a);
-          acc[j * LD_TT + t] = a;
+          acc[j * TT + t] = a;
         }
       }
     }
   }
   int base = 0;
-  reduce_scatter_d<LD_EPW * LD_TT, 32>(acc, lane, base);
-  if ((lane & 1) == 0) {
-    const int j = base / LD_TT, t = base % LD_TT, e = e0 + j;
-    if (t < T && e < E) part[((int64_t)ks * T + t) * E + e] = acc[0];
+  reduce_scatter_d<V, 32>(acc, lane, base);
+  if ((lane & (64 / V - 1)) == 0) {  // each sum is held by 64 / V lanes
+    const int j = base / TT, t = base % TT, e = e0 + j;
+    if (t < nt && e < E) part[((int64_t)ks * T + t0 + t) * E + e] = acc[0];
   }
 }
 
@@ -395,8 +402,16 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid, Sel
   if (T <= LD_TT && H % 256 == 0) {
     // route_ksplit gives 256-wide K chunks here (one float4 per lane and row)
     if (H / ks != 256) return hipErrorInvalidValue;
-    dim3 grid((E + 4 * LD_EPW - 1) / (4 * LD_EPW), ks);
-    hipLaunchKernelGGL(logits_decode_kernel<1>, grid, dim3(256), 0, s, r.x, r.W, T, E, H, r.logits, r.xq, r.xd);
+    const int gx = (E + 4 * LD_EPW - 1) / (4 * LD_EPW);
+    if (T == 1)
+      hipLaunchKernelGGL((logits_decode_kernel<1, 1>), dim3(gx, ks, 1), dim3(256), 0, s, r.x, r.W, T, E, H, r.logits,
+                         r.xq, r.xd);
+    else if (T <= 4)
+      hipLaunchKernelGGL((logits_decode_kernel<1, 4>), dim3(gx, ks, 1), dim3(256), 0, s, r.x, r.W, T, E, H, r.logits,
+                         r.xq, r.xd);
+    else
+      hipLaunchKernelGGL((logits_decode_kernel<1, 8>), dim3(gx, ks, (T + 7) / 8), dim3(256), 0, s, r.x, r.W, T, E, H,
+                         r.logits, r.xq, r.xd);
     x_done = true;
   } else if (T <= LD_TT) {
     dim3 grid((E + 15) / 16, 1, ks);
