@@ -371,7 +371,11 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------------ host side
 int32_t route_ksplit(const coli_moe_cfg &c, int32_t T) {
-  if (T <= LD_TT && c.hidden % 256 == 0) return c.hidden / 256;  // 256-wide K chunks: enough workgroups at decode sizes
+  // decode sizes: 256-wide K chunks give enough workgroups; one token takes 512-wide
+  // chunks, half the partials for the selection inside the gate/up GEMV to sum
+  // (measured: GLM-scale T = 1 45.8 -> 44.5 us per layer)
+  if (T == 1 && c.hidden % 512 == 0) return c.hidden / 512;
+  if (T <= LD_TT && c.hidden % 256 == 0) return c.hidden / 256;
   // larger T: enough K splits for about 512 workgroups of 64 x 64 (tokens x experts)
   const int nkb = c.hidden / 32;
   const int64_t tiles = (int64_t)((c.n_experts + LM_E - 1) / LM_E) * ((T + LM_T - 1) / LM_T);
@@ -400,10 +404,14 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t mid, Sel
   const int ks = r.ksplit;
   bool x_done = false;  // x quantised by the logits kernel
   if (T <= LD_TT && H % 256 == 0) {
-    // route_ksplit gives 256-wide K chunks here (one float4 per lane and row)
-    if (H / ks != 256) return hipErrorInvalidValue;
+    // route_ksplit gives 256-wide K chunks here (one float4 per lane and row), or
+    // 512-wide ones (two) for one token
+    if (H / ks != 256 && !(T == 1 && H / ks == 512)) return hipErrorInvalidValue;
     const int gx = (E + 4 * LD_EPW - 1) / (4 * LD_EPW);
-    if (T == 1)
+    if (H / ks == 512)
+      hipLaunchKernelGGL((logits_decode_kernel<2, 1>), dim3(gx, ks, 1), dim3(256), 0, s, r.x, r.W, T, E, H, r.logits,
+                         r.xq, r.xd);
+    else if (T == 1)
       hipLaunchKernelGGL((logits_decode_kernel<1, 1>), dim3(gx, ks, 1), dim3(256), 0, s, r.x, r.W, T, E, H, r.logits,
                          r.xq, r.xd);
     else if (T <= 4)

@@ -325,8 +325,10 @@ __device__ __forceinline__ void fused_route(const SelectArgs &a, char *dyn, int 
   double *cs = reinterpret_cast<double *>(dyn);
   double *ss = cs + a.T * a.E;
   char *sl = reinterpret_cast<char *>(ss + a.T * a.E);
-  if (a.ksplit > 8)
+  if (a.ksplit > 16)
     fused_scores<1, 24>(a, cs, ss);
+  else if (a.ksplit > 8)
+    fused_scores<1, 16>(a, cs, ss);
   else
     fused_scores<1, 8>(a, cs, ss);
   __syncthreads();
