@@ -118,38 +118,48 @@ def test_glm_prefill_full_sampled_other_scale_formats(env, fmt):
     _run(env, 3, 2048, PREFILL_SAMPLE, **kw)
 
 
-def test_graph_replay_matches_eager(env):
+@pytest.mark.parametrize("T", [1, 4])
+def test_graph_replay_matches_eager(env, T):
     """A captured graph of several layer calls, replayed several times with eager work
-    and synchronisations in between, reproduces the eager results bit for bit."""
+    and synchronisations in between, reproduces the eager results bit for bit: outputs
+    and routes. One token takes the selection inside the gate/up GEMV (no selection
+    launch), four tokens the selection kernel."""
     import torch
     q, _ = env
     wl = gu.workload_cfg(1)
     cfg = q.make_cfg(**wl)
     d = gu.dev()
-    T, L = 4, 3
-    layers, xs, outs = [], [], []
+    L, k = 3, wl["top_k"]
+    layers, xs, outs, idxs, tws = [], [], [], [], []
     for l in range(L):
         seed = synth.workload_seed(1, l)
         inp = synth.layer_inputs(seed, l, tokens=T, hidden=2048, ffn=1024, n_experts=64, has_shared=False, wbits=4)
         layers.append(gu.upload_layer(inp))
         xs.append(gu.to_dev(inp["x"]))
         outs.append(torch.empty((T, 2048), dtype=torch.float32, device=d))
+        idxs.append(torch.empty((T, k), dtype=torch.int32, device=d))
+        tws.append(torch.empty((T, k), dtype=torch.float32, device=d))
     ws = q.alloc_workspace(cfg, T, d)
     eager = []
     for l in range(L):
-        q.layer(cfg, layers[l], xs[l], outs[l], ws)
-        eager.append(outs[l].clone())
+        q.layer(cfg, layers[l], xs[l], outs[l], ws, idxs[l], tws[l])
+        eager.append((outs[l].clone(), idxs[l].clone(), tws[l].clone()))
     torch.cuda.synchronize()
     s = torch.cuda.Stream(d)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for l in range(L):
-            q.layer(cfg, layers[l], xs[l], outs[l], ws, stream=s)
+            q.layer(cfg, layers[l], xs[l], outs[l], ws, idxs[l], tws[l], stream=s)
     for rep in range(4):
-        for o in outs:
-            o.fill_(float("nan"))
+        for l in range(L):
+            outs[l].fill_(float("nan"))
+            idxs[l].fill_(-7)
+            tws[l].fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         for l in range(L):
-            assert torch.equal(outs[l].view(torch.int32), eager[l].view(torch.int32)), (rep, l)
+            eo, ei, ew = eager[l]
+            assert torch.equal(outs[l].view(torch.int32), eo.view(torch.int32)), (rep, l)
+            assert torch.equal(idxs[l], ei), (rep, l)
+            assert torch.equal(tws[l].view(torch.int32), ew.view(torch.int32)), (rep, l)
         _ = torch.randn(1000, device=d).sum().item()  # eager work between replays
