@@ -740,7 +740,9 @@ __device__ __forceinline__ void fast_pass_pl(const FastCtx &c, int nt, int lane,
   constexpr int BPC = Fmt<WB>::BPC;
   constexpr int LPC = Fmt<WB>::CHUNK / 16;
   constexpr int TILE = 4 * WR;
-  constexpr int BR_LOAD = cmin<4, (8 / (NMAT * LPC) > 0 ? 8 / (NMAT * LPC) : 1)>::v;
+  // MXFP4 steps take two rows: its converted codes and fp16 activation pairs need twice
+  // the registers of the integer formats
+  constexpr int BR_LOAD = cmin<(WB == W_MX ? 2 : 4), (8 / (NMAT * LPC) > 0 ? 8 / (NMAT * LPC) : 1)>::v;
   constexpr int BR_ACC = (32 / (NMAT * NTC) > 0) ? 32 / (NMAT * NTC) : 1;
   constexpr int BR_ROWS = (WR / RPI > 0) ? WR / RPI : 1;
   constexpr int BR = cmin<cmin<BR_LOAD, BR_ACC>::v, BR_ROWS>::v;
@@ -833,14 +835,19 @@ __device__ __forceinline__ void fast_pass_pl(const FastCtx &c, int nt, int lane,
 // The pipelined pass where it measured faster and fits three wavefronts per SIMD
 // without spilling: int4 gate/up rows of three chunks per lane with one scale per row
 // (GLM-scale experts). Elsewhere its second register set spills or costs occupancy.
+// MXFP4 gate/up rows of three chunks take it for one-token batches only (`one`; two
+// wavefronts per SIMD, as the plain pass): GLM-scale T = 1 gate/up 38.0 -> 34.9 us,
+// while at T = 4 and 16 it measured slower (84.4 -> 90.1 us, 288.3 -> 305.4 us).
 template <int WB, int CPL, int MODE, bool GS>
 struct FastPl {
   static constexpr bool on = WB == 4 && CPL == 3 && MODE == MODE_GATEUP && !GS;
+  static constexpr bool one = WB == W_MX && CPL == 3 && MODE == MODE_GATEUP;
 };
 
 // GS: one scale per 64 inputs of a row, applied per chunk (see gemv_kernel).
-template <int WB, int LPR, int CPL, int MODE, int WR, bool GS = false>
-__global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void gemv_fast_kernel(FfnArgs a, int ntmax) {
+// PL: every pass takes the pipelined form (fast_pass_pl), bit-identical to fast_pass.
+template <int WB, int LPR, int CPL, int MODE, int WR, bool GS = false, bool PL = FastPl<WB, CPL, MODE, GS>::on>
+__global__ __launch_bounds__(256, (PL ? (WB == 4 ? 3 : 2) : 1)) void gemv_fast_kernel(FfnArgs a, int ntmax) {
   constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int TILE = 4 * WR;
   static_assert(MODE == MODE_DOWN || TILE % QK == 0, "gate/up tiles hold whole Q8_0 blocks of h");
@@ -909,7 +916,7 @@ __global__ __launch_bounds__(256, (FastPl<WB, CPL, MODE, GS>::on ? 3 : 1)) void 
     // a slot with more tokens than one pass takes re-reads its rows on every pass: those
     // loads allocate in L2 so that the later passes find them there
     const bool keep = n > ntmax;
-    if constexpr (FastPl<WB, CPL, MODE, GS>::on) {
+    if constexpr (PL) {
       if (keep)
         fast_pass_pl<WB, NMAT, LPR, CPL, WR, 2, GS, true>(c, nt, lane, wv);
       else if (nt <= 1)
@@ -1505,6 +1512,12 @@ static hipError_t launch_fast(const FfnArgs &a, dim3 slots_grid, int nrows, int 
                                   (size_t)NMAT * 8 * TILE * sizeof(float) + 16 * sizeof(int),
                               fused_lds_bytes(a, true));
   dim3 grid(nrows / TILE, slots_grid.y);
+  if constexpr (FastPl<WB, CPL, MODE, GS>::one) {
+    if (a.T == 1) {
+      hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR, GS, true>), grid, dim3(256), lds, s, a, ntmax);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemv_fast_kernel<WB, LPR, CPL, MODE, WR, GS>), grid, dim3(256), lds, s, a, ntmax);
   return hipGetLastError();
 }
